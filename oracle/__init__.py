@@ -1,0 +1,186 @@
+"""CPU oracle for one mixture-of-experts layer's forward pass.
+
+TEST INFRASTRUCTURE.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its binding) never imports it, and it imports nothing
+from the product path.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, double precision); this
+module builds it with gcc, loads it with ctypes and marshals numpy arrays.
+Array conventions: ``x`` and the expert weights are either ``float32`` arrays
+or ``uint16`` arrays of bfloat16 bit patterns; logits are ``float32``.
+
+Steps and the passages they follow (Hugging Face Transformers docs):
+  route      "Expert parallelism", "Adding an implementation" (top_k_index,
+             top_k_weights); softmax top-k, ties to the lower expert index.
+  dispatch   "Expert parallelism", "Token dispatch": pairs grouped by expert,
+             stable in pair order.
+  experts    "Tensor parallelism for inference", "Packed strategies": packed
+             gate/up weight [E, d, 2I], hidden @ W, gate half first; SwiGLU.
+  combine    "Expert parallelism", "Token dispatch": routing-weighted sum.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC_PATH = os.path.join(_HERE, "moe_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(src: str = SRC_PATH, out: str = LIB_PATH) -> str:
+    """Compile the oracle's C source into a shared library (gcc, -O2, no
+    fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
+           src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _bind(lib):
+    """Declare the C signatures on a loaded copy of the oracle library."""
+    p = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_route.argtypes = [p, i64, i32, i32, p, p]
+    lib.oracle_route.restype = ctypes.c_int
+    lib.oracle_dispatch.argtypes = [p, i64, i32, i32, p, p, p]
+    lib.oracle_dispatch.restype = ctypes.c_int
+    lib.oracle_moe_tokens.argtypes = [p, ctypes.c_int, i64, i32, i32, i32, i32, p, p, p, p, p, i64,
+                                      ctypes.c_int, p, p]
+    lib.oracle_moe_tokens.restype = ctypes.c_int
+    return lib
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"expected float32 or uint16 (bfloat16 bits), got {a.dtype}")
+
+
+def default_threads() -> int:
+    n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def route(logits: np.ndarray, k: int):
+    """Top-k selection and renormalised softmax weights.
+
+    Returns ``(idx int32 [T, k], w float64 [T, k])``; slot 0 holds the largest logit.
+    """
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    rc = _load().oracle_route(_ptr(logits), T, E, k, _ptr(idx), _ptr(w))
+    if rc != 0:
+        raise ValueError(f"oracle_route failed ({rc}): T={T} E={E} k={k}")
+    return idx, w
+
+
+def dispatch(pair_expert: np.ndarray, k: int, E: int):
+    """Stable grouping of pairs by expert.
+
+    ``pair_expert`` [P] holds the expert of pair p = t*k + j, or -1.
+    Returns ``(offsets [E+1], pair_row [P], row_token [offsets[E]])`` (int32).
+    """
+    pe = np.ascontiguousarray(pair_expert, dtype=np.int32).reshape(-1)
+    P = pe.shape[0]
+    offsets = np.empty(E + 1, dtype=np.int32)
+    pair_row = np.empty(P, dtype=np.int32)
+    row_token = np.empty(P, dtype=np.int32)
+    rc = _load().oracle_dispatch(_ptr(pe), P, k, E, _ptr(offsets), _ptr(pair_row), _ptr(row_token))
+    if rc != 0:
+        raise ValueError(f"oracle_dispatch failed ({rc}): P={P} k={k} E={E}")
+    return offsets, pair_row, row_token[: offsets[E]].copy()
+
+
+def permute_rows(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
+    """Expert-ordered copy of the token rows: row r is x[row_token[r]] (a pure byte move)."""
+    return x[np.asarray(row_token, dtype=np.int64)]
+
+
+def moe_tokens(x: np.ndarray, idx: np.ndarray, w: np.ndarray, w_gate_up: np.ndarray,
+               w_down: np.ndarray, tokens=None, nthreads: int | None = None, want_y: bool = False):
+    """Experts + combine for the listed tokens (all tokens when ``tokens`` is None).
+
+    ``out[n] = sum_j w[t, j] * FFN_{idx[t, j]}(x[t])`` for ``t = tokens[n]``, float64.
+    With ``want_y`` also returns ``y_pair [n, k, d]`` = FFN_{idx[t, j]}(x[t]).
+    """
+    dt = _dtype_code(x)
+    if _dtype_code(w_gate_up) != dt or _dtype_code(w_down) != dt:
+        raise TypeError("x and expert weights must share one element type")
+    x = np.ascontiguousarray(x)
+    w_gate_up = np.ascontiguousarray(w_gate_up)
+    w_down = np.ascontiguousarray(w_down)
+    T, d = x.shape
+    E, d2, two_i = w_gate_up.shape
+    I = two_i // 2
+    if d2 != d or two_i != 2 * I or w_down.shape != (E, I, d):
+        raise ValueError(f"shape mismatch: x {x.shape}, w_gate_up {w_gate_up.shape}, w_down {w_down.shape}")
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(T, -1)
+    k = idx.shape[1]
+    w = np.ascontiguousarray(w, dtype=np.float64).reshape(T, k)
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int64)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64).reshape(-1)
+    n = tokens.shape[0]
+    out = np.empty((n, d), dtype=np.float64)
+    y = np.empty((n, k, d), dtype=np.float64) if want_y else None
+    rc = _load().oracle_moe_tokens(_ptr(x), dt, T, d, E, k, I, _ptr(idx), _ptr(w), _ptr(w_gate_up),
+                                   _ptr(w_down), _ptr(tokens), n, nthreads or default_threads(),
+                                   _ptr(out), _ptr(y) if want_y else None)
+    if rc != 0:
+        raise ValueError(f"oracle_moe_tokens failed ({rc})")
+    return (out, y) if want_y else out
+
+
+def forward(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray, k: int, logits=None,
+            pair_expert=None, pair_w=None, tokens=None, nthreads: int | None = None,
+            want_y: bool = False) -> dict:
+    """The whole layer: route (when ``logits`` is given; otherwise the pairs are
+    given as ``pair_expert``/``pair_w``), dispatch, experts, combine.
+
+    Returns a dict with ``idx, w, offsets, pair_row, row_token, out`` (and
+    ``y_pair`` with ``want_y``); ``out`` covers ``tokens`` (default: all).
+    """
+    T = x.shape[0]
+    E = w_gate_up.shape[0]
+    if logits is not None:
+        idx, w = route(logits, k)
+    else:
+        idx = np.asarray(pair_expert, dtype=np.int32).reshape(T, k)
+        w = np.asarray(pair_w, dtype=np.float64).reshape(T, k)
+    offsets, pair_row, row_token = dispatch(idx.reshape(-1), k, E)
+    res = dict(idx=idx, w=w, offsets=offsets, pair_row=pair_row, row_token=row_token)
+    r = moe_tokens(x, idx, w, w_gate_up, w_down, tokens=tokens, nthreads=nthreads, want_y=want_y)
+    if want_y:
+        res["out"], res["y_pair"] = r
+    else:
+        res["out"] = r
+    return res
