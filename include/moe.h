@@ -1,0 +1,144 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts layer library.
+ *
+ * One MoE layer's forward pass on one GPU: route (top-k + renormalised
+ * softmax), permute (group the (token, expert) pairs by expert and copy the
+ * token rows into expert-contiguous order), grouped feed-forward (each
+ * expert's SwiGLU MLP over its own rows) and combine (routing-weighted sum
+ * back to token order).  The operations follow the Hugging Face Transformers
+ * docs, "Expert parallelism" (sections "Adding an implementation" and "Token
+ * dispatch") and "Tensor parallelism for inference" (section "Packed
+ * strategies"); each entry point names its passage.
+ *
+ * Conventions for every entry point:
+ *  - Array arguments are DEVICE pointers (for example a torch tensor's
+ *    data_ptr()).  The caller owns every buffer; the library allocates and
+ *    frees nothing and never synchronises with the host.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  On success the
+ *    work is enqueued on it and MOE_OK is returned at once.  Faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - Scalars and pointers are validated on the host FIRST: on any error a
+ *    status is returned and nothing is enqueued.
+ *  - Rows are row-major and dense (stride = row length).  Element type
+ *    `moe_dtype`: MOE_F32 (IEEE float) or MOE_BF16 (bfloat16).
+ *  - Limits: 1 <= k <= E <= 256; d and I multiples of 64; T*k*max(d, I) and
+ *    every array size below 2^31 elements.  T == 0 is valid (nothing runs).
+ *  - Device-side values that the host cannot see (expert ids, offsets, row
+ *    indices) are clamped to the buffers they index: an expert id outside
+ *    [0, E) drops its pair, a row index outside the capacity is skipped.
+ *    Garbage in such arrays gives garbage results, never an out-of-bounds
+ *    access.
+ *  - Calls are reentrant; concurrent calls need separate workspaces.
+ *  - No call reads device memory from the host, so a sequence of calls can
+ *    be captured into a HIP graph.
+ */
+#ifndef TRE_MOE_H
+#define TRE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,         /* invalid argument: bad size, NULL pointer, k > E ... */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside the library's limits (E > 256, d % 64 ...) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace_size() */
+  MOE_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} moe_status;
+
+/* Static, never NULL. */
+const char* moe_status_string(moe_status s);
+
+/* ---- route ----------------------------------------------------------------
+ * "Expert parallelism", "Adding an implementation": the expert path receives
+ * each token's selected expert ids (top_k_index) and routing weights
+ * (top_k_weights).  Selection rule (softmax top-k): the k largest logits,
+ * equal logits ordered by the lower expert index (-0.0 equals +0.0); slot 0
+ * holds the largest.  Weight of slot j: exp(l_j - l_0) / sum over the k
+ * selected of exp(l_i - l_0), i.e. the softmax probability renormalised over
+ * the selection.
+ *   logits    [T, E] float32, finite
+ *   topk_idx  [T, k] int32  (output)
+ *   topk_w    [T, k] float32 (output)                                        */
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                          int32_t* topk_idx, float* topk_w, void* stream);
+
+/* ---- permute --------------------------------------------------------------
+ * "Expert parallelism", "Token dispatch": every (token, expert) pair goes to
+ * the expert's owner, which runs the expert on the rows it receives.  Here:
+ * pair p = t*k + j with expert pair_expert[p] (-1, or any id outside [0, E):
+ * not handled here, dropped).  Pairs are grouped by expert, stable in p:
+ * expert e owns rows [expert_offsets[e], expert_offsets[e+1]).
+ *   x               [T, d] dt
+ *   pair_expert     [T*k] int32
+ *   x_perm          [T*k, d] dt   (output; rows >= expert_offsets[E] untouched)
+ *   row_token       [T*k] int32   (output; row r holds token row_token[r])
+ *   pair_row        [T*k] int32   (output; row of pair p, -1 when dropped)
+ *   expert_offsets  [E+1] int32   (output)
+ *   workspace       >= moe_permute_workspace_size(T, k, E) bytes, 256-aligned */
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
+moe_status moe_permute(const void* x, moe_dtype dt, int32_t T, int32_t d, int32_t k,
+                       const int32_t* pair_expert, int32_t E, void* x_perm, int32_t* row_token,
+                       int32_t* pair_row, int32_t* expert_offsets, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ---- grouped feed-forward ---------------------------------------------------
+ * "Tensor parallelism for inference", "Packed strategies": gate and up
+ * projections packed as one [E, d, 2I] weight applied as x @ W and split with
+ * the gate half first; down projection [E, I, d] (down_proj, "Expert
+ * parallelism", "Overriding plans"), same orientation.  For each expert e and
+ * each row r in [expert_offsets[e], expert_offsets[e+1]):
+ *   h      = silu(x_perm[r] @ Wgu[e][:, :I]) * (x_perm[r] @ Wgu[e][:, I:])
+ *   y[r]   = h @ Wd[e]
+ * float32 accumulation; h is rounded to dt before the down projection.
+ * Offsets are read on the device only.
+ *   x_perm      [max_rows, d] dt
+ *   w_gate_up   [E, d, 2I] dt;  w_down [E, I, d] dt
+ *   y_perm      [max_rows, d] dt (output; rows >= expert_offsets[E] untouched)
+ *   workspace   >= moe_grouped_ffn_workspace_size(max_rows, E, d, I, dt) bytes */
+size_t moe_grouped_ffn_workspace_size(int32_t max_rows, int32_t E, int32_t d, int32_t I, moe_dtype dt);
+moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, int32_t max_rows,
+                           int32_t E, int32_t d, int32_t I, const void* w_gate_up,
+                           const void* w_down, moe_dtype dt, void* y_perm, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ---- combine ----------------------------------------------------------------
+ * "Expert parallelism", "Token dispatch" / "Adding an implementation": the
+ * expert outputs are combined with the routing weights into the weighted
+ * expert output of each token:
+ *   out[t] = sum over j < k with 0 <= pair_row[t*k+j] < max_rows of
+ *            pair_w[t*k+j] * y_perm[pair_row[t*k+j]]
+ * float32 accumulation in ascending j, rounded to dt.
+ *   y_perm [max_rows, d] dt; pair_row, pair_w [T*k]; out [T, d] dt (output)  */
+moe_status moe_combine(const void* y_perm, int32_t max_rows, const int32_t* pair_row,
+                       const float* pair_w, int32_t T, int32_t k, int32_t d, moe_dtype dt,
+                       void* out, void* stream);
+
+/* ---- the whole layer ----------------------------------------------------------
+ * "Expert parallelism", "Adding an implementation": called with the batch
+ * this device holds and returns the weighted expert output of each token.
+ * logits != NULL: route first (topk_idx / topk_w are outputs).
+ * logits == NULL: topk_idx / topk_w are INPUTS (already-routed pairs, e.g.
+ *   the rows one expert-parallel rank received, ids local to this device).
+ * expert_offsets [E+1], row_token [T*k], pair_row [T*k] are optional outputs
+ * (NULL: kept in the workspace).
+ *   x [T, d] dt; out [T, d] dt (output)
+ *   workspace >= moe_forward_workspace_size(T, d, E, k, I, dt) bytes          */
+size_t moe_forward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, moe_dtype dt);
+moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                       int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt,
+                       int32_t* topk_idx, float* topk_w, int32_t* expert_offsets, int32_t* row_token,
+                       int32_t* pair_row, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRE_MOE_H */

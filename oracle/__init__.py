@@ -184,3 +184,21 @@ def forward(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray, k: int, lo
     else:
         res["out"] = r
     return res
+
+
+def combine(y_perm: np.ndarray, pair_row: np.ndarray, pair_w: np.ndarray, T: int, k: int) -> np.ndarray:
+    """The combine step on its own, for given expert-ordered rows: for each
+    token t, the sum over slots j (ascending) with a row of
+    ``pair_w[t*k+j] * y_perm[pair_row[t*k+j]]``, in float64.  ``y_perm`` is
+    float32 or bf16 bits."""
+    y = y_perm.astype(np.float64) if y_perm.dtype == np.float32 else \
+        (y_perm.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    pair_row = np.asarray(pair_row).reshape(-1)
+    pair_w = np.asarray(pair_w, dtype=np.float64).reshape(-1)
+    out = np.zeros((T, y.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            r = int(pair_row[t * k + j])
+            if 0 <= r < y.shape[0]:
+                out[t] += pair_w[t * k + j] * y[r]
+    return out

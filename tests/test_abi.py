@@ -1,0 +1,96 @@
+"""The C-ABI library: it loads, exports what include/moe.h declares, and its
+host-side validation rejects bad arguments before touching the GPU.
+
+Every call here returns from the host checks, so no kernel is launched and no
+GPU is needed."""
+import ctypes
+
+import pytest
+
+import token_routing_expert_amd as tre
+
+P = ctypes.c_void_p
+FAKE = P(256)  # never dereferenced: every call below fails validation or has nothing to do
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tre.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = tre.exported_symbols()
+    assert set(names) == {
+        "moe_status_string", "moe_route_topk", "moe_permute_workspace_size", "moe_permute",
+        "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
+        "moe_forward_workspace_size", "moe_forward"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_route_validation(lib):
+    f = lib.moe_route_topk
+    assert f(FAKE, 4, 8, 9, FAKE, FAKE, None) == 1          # k > E
+    assert f(FAKE, 4, 8, 0, FAKE, FAKE, None) == 1          # k < 1
+    assert f(FAKE, -1, 8, 2, FAKE, FAKE, None) == 1         # T < 0
+    assert f(FAKE, 4, 257, 2, FAKE, FAKE, None) == 2        # E > 256
+    assert f(FAKE, 4, 0, 1, FAKE, FAKE, None) == 1          # E < 1
+    assert f(None, 4, 8, 2, FAKE, FAKE, None) == 1          # NULL logits
+    assert f(None, 0, 8, 2, None, None, None) == 0          # T == 0: nothing to do
+
+
+def test_permute_validation(lib):
+    f = lib.moe_permute
+    ws = lib.moe_permute_workspace_size(100, 2, 16)
+    assert ws >= 2 * 16 * 4 and ws % 256 == 0
+    assert lib.moe_permute_workspace_size(-1, 2, 16) == 0
+    args = [FAKE, 1, 100, 128, 2, FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+    assert f(*args[:3], 96, *args[4:]) == 2                          # d % 64
+    assert f(*args[:6], 300, *args[7:]) == 2                         # E > 256
+    assert f(*args[:1], 7, *args[2:]) == 1                           # bad dtype
+    assert f(*args[:12], ws - 1, None) == 3                          # small workspace
+    assert f(*args[:5], None, *args[6:]) == 1                        # NULL pair_expert
+    assert f(FAKE, 1, 0, 128, 2, None, 16, None, None, None, FAKE, None, 0, None) == 0   # T == 0
+
+
+def test_grouped_ffn_validation(lib):
+    f = lib.moe_grouped_ffn
+    n = lib.moe_grouped_ffn_workspace_size(1000, 16, 1024, 2816, 1)
+    assert n >= 1000 * 2816 * 2
+    assert lib.moe_grouped_ffn_workspace_size(1000, 16, 1024, 2816, 0) >= 1000 * 2816 * 4
+    base = [FAKE, FAKE, 1000, 16, 1024, 2816, FAKE, FAKE, 1, FAKE, FAKE, n, None]
+    assert f(*base[:5], 2800, *base[6:]) == 2                        # I % 64
+    assert f(*base[:4], 1000, *base[5:]) == 2                        # d % 64
+    assert f(*base[:11], n - 1, None) == 3
+    assert f(*base[:6], None, *base[7:]) == 1                        # NULL weights
+    assert f(*base[:2], 0, *base[3:]) == 0                           # no rows
+    assert f(*base[:2], -5, *base[3:]) == 1
+
+
+def test_combine_validation(lib):
+    f = lib.moe_combine
+    assert f(FAKE, 10, FAKE, FAKE, 5, 2, 100, 1, FAKE, None) == 2    # d % 64
+    assert f(FAKE, 10, FAKE, FAKE, 5, 0, 128, 1, FAKE, None) == 1    # k < 1
+    assert f(FAKE, 10, None, FAKE, 5, 2, 128, 1, FAKE, None) == 1    # NULL pair_row
+    assert f(None, 0, None, None, 0, 2, 128, 1, None, None) == 0     # T == 0
+
+
+def test_forward_validation(lib):
+    f = lib.moe_forward
+    n = lib.moe_forward_workspace_size(64, 128, 8, 2, 256, 0)
+    assert n > 0
+    base = [FAKE, FAKE, 64, 128, 8, 2, 256, FAKE, FAKE, 0, FAKE, FAKE, None, None, None, FAKE, FAKE, n, None]
+    assert f(*base[:5], 9, *base[6:]) == 1                           # routed k > E
+    assert f(*base[:17], n - 1, None) == 3
+    assert f(*base[:6], 100, *base[7:]) == 2                         # I % 64
+    assert f(*base[:4], 300, *base[5:]) == 2                         # E > 256
+    assert f(*base[:15], None, *base[16:]) == 1                      # NULL out
+    assert f(*base[:2], 0, *base[3:]) == 0                           # T == 0
+    # workspace grows with the batch
+    assert lib.moe_forward_workspace_size(128, 128, 8, 2, 256, 0) > n

@@ -230,3 +230,20 @@ def test_forward_wires_the_steps():
     assert np.array_equal(res["offsets"], off) and np.array_equal(res["pair_row"], pr)
     assert np.array_equal(res["row_token"], rt)
     np.testing.assert_array_equal(res["out"], oracle.moe_tokens(inp.x, idx, w, inp.w_gate_up, inp.w_down))
+
+
+def test_combine_step_matches_layer():
+    # rows placed in expert order by the dispatch, then combined on their own,
+    # give the layer's output
+    inp = make_custom(T=30, d=16, E=5, k=3, I=8, dtype="f32", seed=61, logits="normal")
+    res = oracle.forward(inp.x, inp.w_gate_up, inp.w_down, 3, logits=inp.logits, want_y=True)
+    P = 30 * 3
+    y_perm = np.zeros((P, 16), dtype=np.float32)
+    pr = res["pair_row"]
+    for p in range(P):
+        y_perm[pr[p]] = res["y_pair"][p // 3, p % 3]
+    out = oracle.combine(y_perm, pr, res["w"], 30, 3)
+    ref = oracle.combine(y_perm.astype(np.float64).astype(np.float32), pr, res["w"], 30, 3)
+    assert np.array_equal(out, ref)
+    # y_perm holds the expert outputs rounded to float32; the layer keeps doubles
+    np.testing.assert_allclose(out, res["out"], rtol=1e-6, atol=1e-9)

@@ -1,0 +1,377 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: routing indices, expert offsets, the permutation and the moved rows are
+bit-exact; routing weights within 1e-6 absolute; float outputs within a
+relative L2 error of 2e-2 (bf16) or 1e-5 (float32).  Small cases are compared
+element by element over whole tensors; the full-size workloads compare the
+routing and permutation in full and the layer output on sampled tokens, in
+the same launch configuration the benchmark times.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import TOL, as_f64, rel_l2, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+W_TOL = 1e-6
+
+
+@pytest.fixture(scope="module")
+def tre():
+    import torch
+    assert torch.cuda.is_available(), "the GPU tests need an MI355X"
+    import token_routing_expert_amd as m
+    m.load()
+    return m
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def sync():
+    _torch().cuda.synchronize()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- route
+
+def check_route(tre, logits, k):
+    idx, w = tre.moe_route_topk(to_device(logits), k)
+    sync()
+    ref_idx, ref_w = oracle.route(logits, k)
+    got_idx, got_w = to_host(idx), to_host(w)
+    assert np.array_equal(got_idx, ref_idx)
+    assert np.max(np.abs(got_w - ref_w), initial=0) <= W_TOL
+
+
+@pytest.mark.parametrize("E", [1, 5, 8, 16, 31, 64, 100, 128, 200, 256])
+def test_route_ties(tre, E):
+    rng = np.random.default_rng(100 + E)
+    values = np.array([-1.0, 0.0, -0.0, 1.0, 0.5, -0.5, 2.0], dtype=np.float32)
+    logits = values[rng.integers(0, len(values), size=(777, E))]
+    for k in sorted({1, min(2, E), min(4, E), (E + 1) // 2, E}):
+        say(f"route ties E={E} k={k}")
+        check_route(tre, logits, k)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (16, 1), (16, 2), (128, 4), (256, 8), (256, 256), (37, 5)])
+def test_route_random(tre, E, k):
+    rng = np.random.default_rng(E * 1000 + k)
+    logits = (rng.standard_normal((3001, E)) * 3).astype(np.float32)
+    logits[::7, E // 2] = logits[::7, 0]            # exact ties
+    check_route(tre, logits, k)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "large_e128", "decode"])
+def test_route_workloads(tre, name):
+    inp = workloads.make(name, weights=False)
+    say(f"route workload {name}")
+    check_route(tre, inp.logits, inp.k)
+
+
+def test_route_empty(tre):
+    torch = _torch()
+    idx, w = tre.moe_route_topk(torch.zeros((0, 8), dtype=torch.float32, device="cuda"), 2)
+    sync()
+    assert idx.shape == (0, 2)
+
+
+# ---------------------------------------------------------------- permute
+
+def check_permute(tre, x, pair_expert, k, E):
+    torch = _torch()
+    T, d = x.shape
+    P = T * k
+    xd = to_device(x)
+    x_perm = torch.full((P, d), float("nan"), dtype=xd.dtype, device="cuda")
+    x_perm, row_token, pair_row, offsets = tre.moe_permute(xd, to_device(pair_expert), k, E, x_perm=x_perm)
+    sync()
+    sane = np.where((pair_expert >= 0) & (pair_expert < E), pair_expert, -1).astype(np.int32)
+    ref_off, ref_pr, ref_rt = oracle.dispatch(sane, k, E)
+    got_off = to_host(offsets)
+    assert np.array_equal(got_off, ref_off)
+    assert np.array_equal(to_host(pair_row), ref_pr)
+    n = int(ref_off[E])
+    assert np.array_equal(to_host(row_token)[:n], ref_rt)
+    xp = to_host(x_perm)
+    ref_xp = oracle.permute_rows(x, ref_rt)
+    assert np.array_equal(xp[:n].view(np.uint8), ref_xp.view(np.uint8))
+    # rows past the last expert are left untouched
+    assert np.all(np.isnan(as_f64(xp[n:])))
+
+
+@pytest.mark.parametrize("T,k,E,d,dtype", [
+    (3001, 3, 37, 128, "bf16"),     # several chunks, ragged tail
+    (1024, 1, 256, 64, "f32"),      # exactly one chunk, widest E
+    (5, 2, 1, 192, "bf16"),         # one expert
+    (2500, 4, 16, 256, "bf16"),
+])
+def test_permute_random(tre, T, k, E, d, dtype):
+    rng = np.random.default_rng(T + k + E)
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=64, dtype=dtype, seed=7, logits="normal",
+                                weights=False)
+    pe = rng.integers(0, E, size=T * k).astype(np.int32)
+    pe[rng.random(T * k) < 0.1] = -1                 # pairs not handled here
+    say(f"permute T={T} k={k} E={E}")
+    check_permute(tre, inp.x, pe, k, E)
+
+
+def test_permute_out_of_range_ids_are_dropped(tre):
+    rng = np.random.default_rng(3)
+    inp = workloads.make_custom(T=700, d=64, E=12, k=2, I=64, dtype="bf16", seed=3, weights=False)
+    pe = rng.integers(0, 12, size=1400).astype(np.int32)
+    pe[::5] = 12
+    pe[1::7] = 1 << 20
+    pe[2::11] = -9
+    check_permute(tre, inp.x, pe, 2, 12)
+
+
+def test_permute_all_one_expert(tre):
+    inp = workloads.make_custom(T=1500, d=128, E=9, k=2, I=64, dtype="bf16", seed=4, weights=False)
+    check_permute(tre, inp.x, np.full(3000, 6, dtype=np.int32), 2, 9)
+
+
+def test_permute_workload_routing(tre):
+    # full-size routing of the 128-expert workload and the rank-share pairs
+    inp = workloads.make("large_e128", weights=False)
+    idx, _ = oracle.route(inp.logits, inp.k)
+    say("permute large_e128")
+    check_permute(tre, inp.x, idx.reshape(-1), inp.k, inp.E)
+    del inp
+    inp = workloads.make("ep_rank_share", weights=False)
+    say("permute ep_rank_share")
+    check_permute(tre, inp.x, inp.pair_expert, 1, inp.E)
+
+
+# ---------------------------------------------------------------- grouped ffn
+
+def check_grouped_ffn(tre, inp, idx):
+    torch = _torch()
+    k = idx.shape[1]
+    offsets, pair_row, row_token = oracle.dispatch(idx.reshape(-1), k, inp.E)
+    n = int(offsets[-1])
+    P = inp.T * k
+    x_perm = np.zeros((P, inp.d), dtype=inp.x.dtype)
+    x_perm[:n] = oracle.permute_rows(inp.x, row_token)
+    y = torch.full((P, inp.d), float("nan"), dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16,
+                   device="cuda")
+    tre.moe_grouped_ffn(to_device(x_perm), to_device(offsets), to_device(inp.w_gate_up), to_device(inp.w_down),
+                        y_perm=y)
+    sync()
+    _, y_pair = oracle.moe_tokens(inp.x, idx, np.ones(idx.shape), inp.w_gate_up, inp.w_down, want_y=True)
+    ref = np.zeros((n, inp.d))
+    pr = pair_row.reshape(inp.T, k)
+    for t in range(inp.T):
+        for j in range(k):
+            if pr[t, j] >= 0:
+                ref[pr[t, j]] = y_pair[t, j]
+    got = to_host(y)
+    err = rel_l2(got[:n], ref)
+    say(f"  grouped ffn rel_l2={err:.3e}")
+    assert err <= TOL[inp.dtype]
+    assert np.all(np.isnan(as_f64(got[n:])))
+    return err
+
+
+@pytest.mark.parametrize("T,d,E,k,I,dtype", [
+    (300, 256, 5, 2, 320, "bf16"),    # partial gate/up column tile (I % 128 = 64), ragged row tiles
+    (301, 192, 3, 1, 192, "bf16"),    # partial down column tile (d % 256 = 192)
+    (520, 128, 2, 2, 256, "bf16"),    # an expert with several row tiles
+    (64, 128, 8, 2, 256, "f32"),
+    (77, 64, 6, 3, 64, "f32"),
+])
+def test_grouped_ffn_random(tre, T, d, E, k, I, dtype):
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype=dtype, seed=T + d, logits="normal_bias")
+    idx, _ = oracle.route(inp.logits, k)
+    say(f"grouped ffn T={T} d={d} E={E} k={k} I={I} {dtype}")
+    check_grouped_ffn(tre, inp, idx)
+
+
+def test_grouped_ffn_empty_experts(tre):
+    inp = workloads.make_custom(T=200, d=128, E=16, k=2, I=128, dtype="bf16", seed=5, logits="normal")
+    idx = np.where(np.arange(400).reshape(200, 2) % 2 == 0, 3, 11).astype(np.int32)   # only experts 3, 11
+    check_grouped_ffn(tre, inp, idx)
+
+
+# ---------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("T,k,d,dtype", [(1000, 4, 256, "bf16"), (333, 2, 64, "f32"), (50, 8, 2880, "bf16")])
+def test_combine_random(tre, T, k, d, dtype):
+    rng = np.random.default_rng(T * k)
+    R = T * k
+    yf = rng.standard_normal((R, d)).astype(np.float32)
+    y = yf if dtype == "f32" else workloads.bf16_bits(yf)
+    pair_row = rng.permutation(R).astype(np.int32)
+    pair_row[rng.random(R) < 0.15] = -1
+    pair_row[::13] = R + 5                                   # outside the rows: skipped
+    w = rng.random(R).astype(np.float32)
+    out = tre.moe_combine(to_device(y), to_device(pair_row), to_device(w), T, k)
+    sync()
+    ref = oracle.combine(y, pair_row, w, T, k)
+    err = rel_l2(to_host(out), ref)
+    assert err <= (TOL[dtype] if dtype == "bf16" else 1e-6), err
+
+
+# ---------------------------------------------------------------- whole layer
+
+def run_forward(tre, inp, stream=None):
+    torch = _torch()
+    T, k, E = inp.T, inp.k, inp.E
+    x = to_device(inp.x)
+    wgu, wd = to_device(inp.w_gate_up), to_device(inp.w_down)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pair_row = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    row_token = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    out = torch.full((T, inp.d), float("nan"), dtype=x.dtype, device="cuda")
+    if inp.logits is not None:
+        res = tre.moe_forward(x, wgu, wd, k, logits=to_device(inp.logits), out=out, expert_offsets=offsets,
+                              pair_row=pair_row, row_token=row_token, stream=stream)
+    else:
+        res = tre.moe_forward(x, wgu, wd, k, topk_idx=to_device(inp.pair_expert.reshape(T, k)),
+                              topk_w=to_device(inp.pair_w.reshape(T, k)), out=out, expert_offsets=offsets,
+                              pair_row=pair_row, row_token=row_token, stream=stream)
+    torch.cuda.synchronize()
+    del x, wgu, wd
+    return dict(out=to_host(res[0]), idx=to_host(res[1]), w=to_host(res[2]), offsets=to_host(offsets),
+                pair_row=to_host(pair_row), row_token=to_host(row_token))
+
+
+def check_forward(tre, inp, tokens=None):
+    got = run_forward(tre, inp)
+    k = inp.k
+    if inp.logits is not None:
+        ref_idx, ref_w = oracle.route(inp.logits, k)
+        assert np.array_equal(got["idx"], ref_idx)
+        assert np.max(np.abs(got["w"] - ref_w)) <= W_TOL
+    else:
+        ref_idx = inp.pair_expert.reshape(inp.T, k)
+        ref_w = inp.pair_w.reshape(inp.T, k).astype(np.float64)
+    sane = np.where((ref_idx >= 0) & (ref_idx < inp.E), ref_idx, -1).astype(np.int32)
+    off, pr, rt = oracle.dispatch(sane.reshape(-1), k, inp.E)
+    assert np.array_equal(got["offsets"], off)
+    assert np.array_equal(got["pair_row"], pr)
+    assert np.array_equal(got["row_token"][: off[-1]], rt)
+    out = got["out"]
+    assert not np.any(np.isnan(as_f64(out)))
+    sel = np.arange(inp.T) if tokens is None else np.asarray(tokens)
+    ref = oracle.moe_tokens(inp.x, sane, ref_w, inp.w_gate_up, inp.w_down, tokens=sel)
+    err = rel_l2(out[sel], ref)
+    say(f"  {inp.name}: out rel_l2={err:.3e} over {len(sel)} tokens")
+    assert err <= TOL[inp.dtype]
+    return got
+
+
+def test_forward_tiny_f32(tre):
+    check_forward(tre, workloads.make("tiny_f32"))
+
+
+def test_forward_small_bf16(tre):
+    inp = workloads.make("small_bf16")
+    say("forward small_bf16 (full oracle)")
+    check_forward(tre, inp)
+
+
+def sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n, replace=False)]))
+
+
+def test_forward_large_e128(tre):
+    inp = workloads.make("large_e128")
+    say("forward large_e128 (sampled tokens)")
+    check_forward(tre, inp, tokens=sample_tokens(inp.T, 40, 1))
+    del inp
+    gc.collect()
+
+
+def test_forward_ep_rank_share(tre):
+    inp = workloads.make("ep_rank_share")
+    say("forward ep_rank_share (sampled rows)")
+    # include rows of the smallest and largest experts
+    counts = np.bincount(inp.pair_expert, minlength=inp.E)
+    live = np.nonzero(counts)[0]
+    extra = [int(np.nonzero(inp.pair_expert == live[np.argmin(counts[live])])[0][0]),
+             int(np.nonzero(inp.pair_expert == np.argmax(counts))[0][0])]
+    check_forward(tre, inp, tokens=np.unique(np.concatenate([sample_tokens(inp.T, 60, 2), extra])))
+    del inp
+    gc.collect()
+
+
+def test_forward_decode(tre):
+    inp = workloads.make("decode")
+    say("forward decode (full oracle)")
+    check_forward(tre, inp)
+    del inp
+    gc.collect()
+
+
+@pytest.mark.parametrize("T,d,E,k,I,dtype,logits", [
+    (1, 128, 16, 1, 128, "bf16", "normal"),          # a single token
+    (5, 64, 256, 8, 64, "bf16", "normal"),           # most experts empty, widest E
+    (130, 128, 4, 4, 192, "bf16", "normal"),         # k = E
+    (257, 64, 3, 2, 64, "f32", "uniform"),
+    (1000, 192, 7, 3, 320, "bf16", "normal_bias"),
+])
+def test_forward_shapes(tre, T, d, E, k, I, dtype, logits):
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype=dtype, seed=T + E, logits=logits)
+    say(f"forward T={T} d={d} E={E} k={k} I={I} {dtype}")
+    check_forward(tre, inp)
+
+
+def test_forward_all_tokens_one_expert(tre):
+    inp = workloads.make_custom(T=700, d=128, E=4, k=1, I=128, dtype="bf16", seed=9, logits="normal")
+    inp.logits[:, 2] += 100.0
+    got = check_forward(tre, inp)
+    assert got["offsets"].tolist() == [0, 0, 0, 700, 700]
+
+
+def test_forward_equal_logits_k_equals_e_is_mean(tre):
+    inp = workloads.make_custom(T=96, d=64, E=4, k=4, I=64, dtype="f32", seed=11, logits="normal")
+    inp.logits[:] = 0.5
+    got = check_forward(tre, inp)
+    assert np.all(got["w"] == np.float32(0.25))
+
+
+def test_forward_given_pairs_with_masked(tre):
+    inp = workloads.make_custom(T=600, d=128, E=16, k=1, I=128, dtype="bf16", seed=13, logits=None,
+                                zero_experts=3)
+    inp.pair_expert[::9] = -1
+    check_forward(tre, inp)
+
+
+def test_forward_zero_rows_give_zero(tre):
+    inp = workloads.make_custom(T=64, d=128, E=8, k=2, I=128, dtype="bf16", seed=15, logits="normal")
+    inp.x[[3, 40]] = 0
+    got = run_forward(tre, inp)
+    assert np.all(got["out"][[3, 40]] == 0)
+
+
+def test_forward_deterministic_and_stream(tre):
+    torch = _torch()
+    inp = workloads.make_custom(T=2048, d=256, E=16, k=2, I=384, dtype="bf16", seed=17, logits="normal_bias")
+    a = run_forward(tre, inp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_forward(tre, inp, stream=s)
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+def test_forward_empty_batch(tre):
+    torch = _torch()
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    wgu = torch.zeros((4, 128, 256), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((4, 128, 128), dtype=torch.bfloat16, device="cuda")
+    out, idx, w = tre.moe_forward(x, wgu, wd, 2, logits=torch.zeros((0, 4), dtype=torch.float32, device="cuda"))
+    sync()
+    assert out.shape == (0, 128)

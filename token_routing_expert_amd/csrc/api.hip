@@ -1,0 +1,192 @@
+// api.hip -- the C ABI (include/moe.h): host-side validation, workspace
+// carving and kernel launches.  Every argument is checked before anything
+// is enqueued; no call allocates, frees or synchronises.
+#include "../../include/moe.h"
+#include "common.hpp"
+
+using namespace tre;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // per-array element limit
+
+size_t elem_size(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_experts(int32_t E) {
+  if (E < 1) return MOE_ERR_ARG;
+  if (E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_width(int32_t n) {
+  if (n < 1) return MOE_ERR_ARG;
+  if (n % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+#define TRY(expr)                    \
+  do {                               \
+    const moe_status st_ = (expr);   \
+    if (st_ != MOE_OK) return st_;   \
+  } while (0)
+
+// Byte layout of the moe_forward workspace.
+struct ForwardLayout {
+  size_t pair_row, row_token, offsets, x_perm, h, y_perm, perm_ws, total;
+};
+
+ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, moe_dtype dt) {
+  const int64_t P = T * k;
+  const size_t s = elem_size(dt);
+  ForwardLayout L;
+  size_t o = 0;
+  L.pair_row = o;  o += align256(P * 4);
+  L.row_token = o; o += align256(P * 4);
+  L.offsets = o;   o += align256((E + 1) * 4);
+  L.x_perm = o;    o += align256(P * d * s);
+  L.h = o;         o += align256(P * I * s);
+  L.y_perm = o;    o += align256(P * d * s);
+  L.perm_ws = o;   o += permute_index_workspace(P, (int)E);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size (limits: E <= 256, d and I multiples of 64)";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                          float* topk_w, void* stream) {
+  if (T < 0) return MOE_ERR_ARG;
+  TRY(check_experts(E));
+  if (k < 1 || k > E) return MOE_ERR_ARG;
+  if ((int64_t)T * E >= kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_ARG;
+  return from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return permute_index_workspace((int64_t)T * k, E);
+}
+
+moe_status moe_permute(const void* x, moe_dtype dt, int32_t T, int32_t d, int32_t k, const int32_t* pair_expert,
+                       int32_t E, void* x_perm, int32_t* row_token, int32_t* pair_row, int32_t* expert_offsets,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt) || T < 0 || k < 1) return MOE_ERR_ARG;
+  TRY(check_experts(E));
+  TRY(check_width(d));
+  const int64_t P = (int64_t)T * k;
+  if (P * d >= kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if (!expert_offsets) return MOE_ERR_ARG;
+  if (T > 0 && (!x || !pair_expert || !x_perm || !row_token || !pair_row)) return MOE_ERR_ARG;
+  if (workspace_bytes < moe_permute_workspace_size(T, k, E) || (T > 0 && !workspace)) return MOE_ERR_WORKSPACE;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  TRY(from_hip(launch_permute_index(pair_expert, P, k, E, row_token, pair_row, expert_offsets, workspace, s)));
+  return from_hip(launch_move_rows(x, T, (int64_t)d * elem_size(dt), row_token, expert_offsets, E, P, x_perm, s));
+}
+
+size_t moe_grouped_ffn_workspace_size(int32_t max_rows, int32_t E, int32_t d, int32_t I, moe_dtype dt) {
+  (void)E;
+  (void)d;
+  if (max_rows < 0 || I < 1 || !dtype_ok(dt)) return 0;
+  return align256((size_t)max_rows * I * elem_size(dt));
+}
+
+moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, int32_t max_rows, int32_t E,
+                           int32_t d, int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt,
+                           void* y_perm, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt) || max_rows < 0) return MOE_ERR_ARG;
+  TRY(check_experts(E));
+  TRY(check_width(d));
+  TRY(check_width(I));
+  if ((int64_t)max_rows * (d > I ? d : I) >= kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)E * d * 2 * I >= 8 * kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if (max_rows == 0) return MOE_OK;
+  if (!x_perm || !expert_offsets || !w_gate_up || !w_down || !y_perm) return MOE_ERR_ARG;
+  if (!workspace || workspace_bytes < moe_grouped_ffn_workspace_size(max_rows, E, d, I, dt)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == MOE_BF16)
+    return from_hip(launch_grouped_ffn_bf16((const bf16_t*)x_perm, expert_offsets, max_rows, E, d, I,
+                                            (const bf16_t*)w_gate_up, (const bf16_t*)w_down, (bf16_t*)workspace,
+                                            (bf16_t*)y_perm, s));
+  return from_hip(launch_grouped_ffn_f32((const float*)x_perm, expert_offsets, max_rows, E, d, I,
+                                         (const float*)w_gate_up, (const float*)w_down, (float*)workspace,
+                                         (float*)y_perm, s));
+}
+
+moe_status moe_combine(const void* y_perm, int32_t max_rows, const int32_t* pair_row, const float* pair_w,
+                       int32_t T, int32_t k, int32_t d, moe_dtype dt, void* out, void* stream) {
+  if (!dtype_ok(dt) || T < 0 || k < 1 || max_rows < 0) return MOE_ERR_ARG;
+  TRY(check_width(d));
+  if ((int64_t)T * k * d >= kMaxElems || (int64_t)max_rows * d >= kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!pair_row || !pair_w || !out || (max_rows > 0 && !y_perm)) return MOE_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == MOE_BF16)
+    return from_hip(launch_combine_bf16((const bf16_t*)y_perm, max_rows, pair_row, pair_w, T, k, d, (bf16_t*)out, s));
+  return from_hip(launch_combine_f32((const float*)y_perm, max_rows, pair_row, pair_w, T, k, d, (float*)out, s));
+}
+
+size_t moe_forward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, moe_dtype dt) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || I < 1 || !dtype_ok(dt)) return 0;
+  return forward_layout(T, d, E, k, I, dt).total;
+}
+
+moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
+                       const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt) || T < 0 || k < 1) return MOE_ERR_ARG;
+  TRY(check_experts(E));
+  if (logits && k > E) return MOE_ERR_ARG;
+  TRY(check_width(d));
+  TRY(check_width(I));
+  const int64_t P = (int64_t)T * k;
+  if (P * (d > I ? d : I) >= kMaxElems || (int64_t)T * E >= kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)E * d * 2 * I >= 8 * kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate_up || !w_down || !topk_idx || !topk_w || !out) return MOE_ERR_ARG;
+  const ForwardLayout L = forward_layout(T, d, E, k, I, dt);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  char* ws = (char*)workspace;
+  int32_t* p_row = pair_row ? pair_row : (int32_t*)(ws + L.pair_row);
+  int32_t* r_tok = row_token ? row_token : (int32_t*)(ws + L.row_token);
+  int32_t* offs = expert_offsets ? expert_offsets : (int32_t*)(ws + L.offsets);
+  void* x_perm = ws + L.x_perm;
+  void* h = ws + L.h;
+  void* y_perm = ws + L.y_perm;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
+  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s)));
+  TRY(from_hip(launch_move_rows(x, T, (int64_t)d * elem_size(dt), r_tok, offs, E, P, x_perm, s)));
+  if (dt == MOE_BF16) {
+    TRY(from_hip(launch_grouped_ffn_bf16((const bf16_t*)x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up,
+                                         (const bf16_t*)w_down, (bf16_t*)h, (bf16_t*)y_perm, s)));
+    return from_hip(launch_combine_bf16((const bf16_t*)y_perm, P, p_row, topk_w, T, k, d, (bf16_t*)out, s));
+  }
+  TRY(from_hip(launch_grouped_ffn_f32((const float*)x_perm, offs, P, E, d, I, (const float*)w_gate_up,
+                                      (const float*)w_down, (float*)h, (float*)y_perm, s)));
+  return from_hip(launch_combine_f32((const float*)y_perm, P, p_row, topk_w, T, k, d, (float*)out, s));
+}
+
+}  // extern "C"

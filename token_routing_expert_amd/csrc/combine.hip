@@ -1,0 +1,108 @@
+// combine.hip -- routing-weighted sum of the expert outputs, back in token order.
+//
+// "Expert parallelism" (Hugging Face Transformers docs), sections "Token
+// dispatch" and "Adding an implementation": the expert outputs of a token
+// are combined with its routing weights into the token's weighted expert
+// output:
+//   out[t] = sum over j < k (pair_row[t*k+j] valid) of pair_w[t*k+j] * y_perm[pair_row[t*k+j]]
+// float32 accumulation in ascending j, one rounding to the output type.
+//
+// One wave per token; lanes walk the row in 16-byte vectors, so each of the
+// k gathered rows is read with full 16-byte coalescing and the output row is
+// written once.  Bandwidth-bound: reads P rows, writes T rows.
+#include "common.hpp"
+
+namespace tre {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename Elem>
+struct Vec;  // one 16-byte vector of Elem and its float32 expansion
+template <>
+struct Vec<bf16_t> {
+  static constexpr int n = 8;
+  static __device__ __forceinline__ void load(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __builtin_bit_cast(float, v[i] << 16);
+      f[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ u32x4 store(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+    return v;
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int n = 4;
+  static __device__ __forceinline__ void load(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // copy the element out first: clang's bit_cast of a vector-element
+      // lvalue reads element 0 whatever the index
+      const uint32_t u = v[i];
+      f[i] = __builtin_bit_cast(float, u);
+    }
+  }
+  static __device__ __forceinline__ u32x4 store(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(uint32_t, f[i]);
+    return v;
+  }
+};
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void k_combine(const u32x4* __restrict__ y, int64_t max_rows,
+                                                      const int32_t* __restrict__ pair_row,
+                                                      const float* __restrict__ pair_w, int64_t n_tok, int k,
+                                                      int64_t vec_per_row, u32x4* __restrict__ out) {
+  constexpr int n = Vec<Elem>::n;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= n_tok) return;
+  const int lane = threadIdx.x % kWave;
+  for (int64_t v = lane; v < vec_per_row; v += kWave) {
+    float acc[n];
+#pragma unroll
+    for (int i = 0; i < n; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = pair_row[t * k + j];
+      if (r < 0 || r >= max_rows) continue;
+      const float w = pair_w[t * k + j];
+      float f[n];
+      Vec<Elem>::load(y[r * vec_per_row + v], f);
+#pragma unroll
+      for (int i = 0; i < n; ++i) acc[i] = fmaf(w, f[i], acc[i]);
+    }
+    out[t * vec_per_row + v] = Vec<Elem>::store(acc);
+  }
+}
+
+template <typename Elem>
+hipError_t launch(const Elem* y, int64_t max_rows, const int32_t* pair_row, const float* pair_w, int64_t n_tok,
+                  int k, int d, Elem* out, hipStream_t s) {
+  const int64_t vec_per_row = (int64_t)d * sizeof(Elem) / 16;
+  const int64_t blocks = ceil_div(n_tok, kThreads / kWave);
+  k_combine<Elem><<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)y, max_rows, pair_row, pair_w, n_tok, k,
+                                                       vec_per_row, (u32x4*)out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine_bf16(const bf16_t* y_perm, int64_t max_rows, const int32_t* pair_row,
+                               const float* pair_w, int64_t T, int k, int d, bf16_t* out, hipStream_t s) {
+  return launch<bf16_t>(y_perm, max_rows, pair_row, pair_w, T, k, d, out, s);
+}
+
+hipError_t launch_combine_f32(const float* y_perm, int64_t max_rows, const int32_t* pair_row,
+                              const float* pair_w, int64_t T, int k, int d, float* out, hipStream_t s) {
+  return launch<float>(y_perm, max_rows, pair_row, pair_w, T, k, d, out, s);
+}
+
+}  // namespace tre

@@ -1,0 +1,69 @@
+// common.hpp -- shared device helpers and internal launcher declarations of
+// the gfx950 MoE library.  Not part of the public ABI (include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tre {
+
+constexpr int kWave = 64;      // CDNA wavefront width
+constexpr int kMaxExperts = 256;
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+
+template <typename T>
+__device__ __forceinline__ T clampi(T v, T lo, T hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// ---- launchers (each returns hipGetLastError() of its launches) ----------
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                             float* topk_w, hipStream_t s);
+
+// Stable grouping of pairs by expert.  Chunk size of the histogram/scatter.
+constexpr int kPermuteChunk = 1024;
+size_t permute_index_workspace(int64_t P, int E);
+hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E,
+                                int32_t* row_token, int32_t* pair_row, int32_t* expert_offsets,
+                                void* ws, hipStream_t s);
+// x_perm[r] = x[row_token[r]] for r < expert_offsets[E]; row_bytes % 16 == 0.
+hipError_t launch_move_rows(const void* x, int64_t T, int64_t row_bytes, const int32_t* row_token,
+                            const int32_t* expert_offsets, int E, int64_t max_rows, void* x_perm,
+                            hipStream_t s);
+
+// Grouped SwiGLU feed-forward.  h: [max_rows, I] scratch of the activation type.
+hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets,
+                                   int64_t max_rows, int E, int d, int I, const bf16_t* w_gate_up,
+                                   const bf16_t* w_down, bf16_t* h, bf16_t* y_perm, hipStream_t s);
+hipError_t launch_grouped_ffn_f32(const float* x_perm, const int32_t* expert_offsets,
+                                  int64_t max_rows, int E, int d, int I, const float* w_gate_up,
+                                  const float* w_down, float* h, float* y_perm, hipStream_t s);
+
+hipError_t launch_combine_bf16(const bf16_t* y_perm, int64_t max_rows, const int32_t* pair_row,
+                               const float* pair_w, int64_t T, int k, int d, bf16_t* out,
+                               hipStream_t s);
+hipError_t launch_combine_f32(const float* y_perm, int64_t max_rows, const int32_t* pair_row,
+                              const float* pair_w, int64_t T, int k, int d, float* out,
+                              hipStream_t s);
+
+}  // namespace tre

@@ -1,0 +1,193 @@
+// permute.hip -- group (token, expert) pairs by expert and move token rows.
+//
+// "Expert parallelism" (Hugging Face Transformers docs), section "Token
+// dispatch": each (token, expert) pair is sent to the expert's owner, which
+// runs the expert on the rows it received.  On one device this is a stable
+// counting sort of the pairs by expert followed by a row gather:
+//   expert e owns rows [offsets[e], offsets[e+1]) in increasing pair order,
+//   row_token[r] = token of row r, pair_row[p] = row of pair p (-1: dropped),
+//   x_perm[r] = x[row_token[r]].
+//
+// Three index kernels, all deterministic (no order-dependent atomics):
+//   hist     one workgroup per chunk of kPermuteChunk pairs counts its pairs
+//            per expert in LDS (counts do not depend on atomic order);
+//   scan     one workgroup turns the per-chunk counts into expert offsets and
+//            each chunk's starting row per expert;
+//   scatter  each chunk walks its pairs in order, 256 at a time: a pair's row
+//            is its chunk's running row for the expert, plus the matching
+//            pairs in earlier waves of the step, plus its rank among equal
+//            experts in its own wave (eight ballots over the expert id bits).
+// The row move is a separate, bandwidth-bound kernel: one wave per
+// destination row, 16-byte vectors, rows written in order.
+#include "common.hpp"
+
+namespace tre {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void k_perm_hist(const int32_t* __restrict__ pair_expert, int64_t P,
+                                                        int E, int32_t* __restrict__ chunk_count) {
+  __shared__ int cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kPermuteChunk;
+  for (int i = tid; i < kPermuteChunk; i += kThreads) {
+    const int64_t p = base + i;
+    if (p < P) {
+      const int e = pair_expert[p];
+      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  if (tid < E) chunk_count[(int64_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+// Exclusive prefix over the 256 threads of a block; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    before += (w < wave) ? s_wave[w] : 0;
+    all += s_wave[w];
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_perm_scan(const int32_t* __restrict__ chunk_count, int n_chunks,
+                                                        int E, int32_t* __restrict__ chunk_base,
+                                                        int32_t* __restrict__ offsets) {
+  __shared__ int s_wave[kThreads / kWave];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int b = 0; b < n_chunks; ++b) total += chunk_count[(int64_t)b * E + e];
+  int all = 0;
+  const int start = block_exclusive_scan(e < E ? total : 0, s_wave, &all);
+  if (e < E) {
+    offsets[e] = start;
+    int run = start;
+    for (int b = 0; b < n_chunks; ++b) {
+      chunk_base[(int64_t)b * E + e] = run;
+      run += chunk_count[(int64_t)b * E + e];
+    }
+  }
+  if (e == 0) offsets[E] = all;
+}
+
+__global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __restrict__ pair_expert, int64_t P,
+                                                           int k, int E,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ pair_row,
+                                                           int32_t* __restrict__ row_token) {
+  __shared__ int running[kMaxExperts];
+  __shared__ int wave_count[kThreads / kWave][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  if (tid < E) running[tid] = chunk_base[(int64_t)blockIdx.x * E + tid];
+  const int64_t base = (int64_t)blockIdx.x * kPermuteChunk;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int step = 0; step < kPermuteChunk; step += kThreads) {
+    if (tid < E) {
+#pragma unroll
+      for (int w = 0; w < kThreads / kWave; ++w) wave_count[w][tid] = 0;
+    }
+    __syncthreads();
+    const int64_t p = base + step + tid;
+    const int e = (p < P) ? pair_expert[p] : -1;
+    const bool valid = e >= 0 && e < E;
+    // lanes of this wave holding the same expert: eight ballots over the id bits
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t b = __ballot(set);
+      peers &= set ? b : ~b;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) wave_count[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int r = running[e] + rank;
+      for (int w = 0; w < wave; ++w) r += wave_count[w][e];
+      pair_row[p] = r;
+      if (r >= 0 && r < P) row_token[r] = (int32_t)(p / k);
+    } else if (p < P) {
+      pair_row[p] = -1;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int add = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / kWave; ++w) add += wave_count[w][tid];
+      running[tid] += add;
+    }
+    // the next step's zeroing is ordered after this update by its own barrier
+    __syncthreads();
+  }
+}
+
+// One wave per destination row; the rows past offsets[E] are left alone.
+__global__ __launch_bounds__(kThreads) void k_move_rows(const u32x4* __restrict__ x, int64_t T, int64_t vec_per_row,
+                                                        const int32_t* __restrict__ row_token,
+                                                        const int32_t* __restrict__ offsets, int E,
+                                                        int64_t max_rows, u32x4* __restrict__ x_perm) {
+  const int64_t n_rows = clampi<int64_t>(offsets[E], 0, max_rows);
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (r >= n_rows) return;
+  const int64_t t = row_token[r];
+  if (t < 0 || t >= T) return;
+  const u32x4* src = x + t * vec_per_row;
+  u32x4* dst = x_perm + r * vec_per_row;
+  const int lane = threadIdx.x % kWave;
+  int64_t v = lane;
+  for (; v + 3 * kWave < vec_per_row; v += 4 * kWave) {
+    const u32x4 a = src[v], b = src[v + kWave], c = src[v + 2 * kWave], d = src[v + 3 * kWave];
+    dst[v] = a;
+    dst[v + kWave] = b;
+    dst[v + 2 * kWave] = c;
+    dst[v + 3 * kWave] = d;
+  }
+  for (; v < vec_per_row; v += kWave) dst[v] = src[v];
+}
+
+}  // namespace
+
+size_t permute_index_workspace(int64_t P, int E) {
+  const int64_t n_chunks = ceil_div(P, kPermuteChunk);
+  return (size_t)round_up(2 * n_chunks * E * (int64_t)sizeof(int32_t), 256);
+}
+
+hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E, int32_t* row_token,
+                                int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s) {
+  const int n_chunks = (int)ceil_div(P, kPermuteChunk);
+  int32_t* chunk_count = (int32_t*)ws;
+  int32_t* chunk_base = chunk_count + (int64_t)n_chunks * E;
+  k_perm_hist<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, E, chunk_count);
+  k_perm_scan<<<1, kThreads, 0, s>>>(chunk_count, n_chunks, E, chunk_base, expert_offsets);
+  k_perm_scatter<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, k, E, chunk_base, pair_row, row_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_move_rows(const void* x, int64_t T, int64_t row_bytes, const int32_t* row_token,
+                            const int32_t* expert_offsets, int E, int64_t max_rows, void* x_perm,
+                            hipStream_t s) {
+  const int rows_per_block = kThreads / kWave;
+  const int64_t blocks = ceil_div(max_rows, rows_per_block);
+  k_move_rows<<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)x, T, row_bytes / 16, row_token,
+                                                    expert_offsets, E, max_rows, (u32x4*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace tre
