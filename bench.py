@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark: one MoE layer forward pass on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input,
+with every input already resident in HBM: route (top-k + renormalised
+softmax) -> permute (group pairs by expert, move rows) -> gate/up projection
+with SwiGLU -> down projection -> combine.  Each stage is one C-ABI call of
+libmoe.so on torch's current stream; HIP events on that stream bracket every
+stage, so each stage's average duration is measured live over the timed
+region.
+
+Prints ONE JSON line.  ``value`` = routed (token, expert) pairs per second of
+the whole layer.  ``roofline`` describes the dominant kernel (the gate/up
+grouped GEMM: algorithmic flops per launch / measured launch duration against
+the MI355X dense bf16 MFMA peak).  ``cpu_baseline`` is the CPU oracle timed on
+a bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "routed token-expert pairs/sec per MoE layer; % bf16 MFMA peak; permute GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up.json")
+GEMM_SOURCE = os.path.join(ROOT, "token_routing_expert_amd", "csrc", "grouped_ffn.hip")
+STAGES = ["route", "permute", "gate_up", "down", "combine"]
+
+
+def kernel_source_hash() -> str:
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def to_device(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def algorithmic_work(inp, n_rows: int, live_experts: int):
+    """Per-launch algorithmic bytes / flops of each stage (what the method must
+    move or compute, not what a kernel happens to touch)."""
+    T, d, E, k, I = inp.T, inp.d, inp.E, inp.k, inp.I
+    s = 4 if inp.dtype == "f32" else 2
+    P = T * k
+    return {
+        "route": {"bytes": (4 * T * E + 8 * P) if inp.logits is not None else 0},
+        "permute": {"bytes": T * d * s + n_rows * d * s + 16 * P},
+        "gate_up": {"flops": 4 * n_rows * d * I,
+                    "bytes": live_experts * 2 * d * I * s + n_rows * d * s + n_rows * I * s},
+        "down": {"flops": 2 * n_rows * I * d,
+                 "bytes": live_experts * d * I * s + n_rows * I * s + n_rows * d * s},
+        "combine": {"bytes": n_rows * d * s + T * d * s + 8 * P},
+    }
+
+
+def cpu_baseline(inp, seconds: float):
+    """Time the CPU oracle on a bounded sample of the workload."""
+    import oracle
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(12345)
+    t0 = time.perf_counter()
+    if inp.logits is not None:
+        idx, w = oracle.route(inp.logits, inp.k)
+    else:
+        idx = inp.pair_expert.reshape(inp.T, inp.k)
+        w = inp.pair_w.reshape(inp.T, inp.k).astype(np.float64)
+    oracle.dispatch(idx.reshape(-1), inp.k, inp.E)
+    t_index = time.perf_counter() - t0
+    probe = rng.choice(inp.T, size=min(inp.T, max(threads, 4)), replace=False)
+    t0 = time.perf_counter()
+    oracle.moe_tokens(inp.x, idx, w, inp.w_gate_up, inp.w_down, tokens=probe, nthreads=threads)
+    per_tok = (time.perf_counter() - t0) / len(probe)
+    n = int(min(inp.T, max(len(probe), (seconds - t_index) / max(per_tok, 1e-9))))
+    sample = np.sort(rng.choice(inp.T, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.moe_tokens(inp.x, idx, w, inp.w_gate_up, inp.w_down, tokens=sample, nthreads=threads)
+    t_ffn = time.perf_counter() - t0
+    # the index work is charged in proportion to the sample
+    t_total = t_ffn + t_index * n / inp.T
+    return {
+        "value": n * inp.k / t_total,
+        "unit": "pairs/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} of {inp.T} tokens ({n * inp.k} pairs) through experts+combine in float64, "
+                  f"plus route+dispatch over all tokens charged pro rata; {t_total:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=workloads.ORDER[1], choices=workloads.ORDER)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB (a known-size "
+                         "reference for HBM byte counters under rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer has no "
+              "multi-GPU path in this build", file=sys.stderr)
+        return 2
+
+    import torch
+    import token_routing_expert_amd as tre
+
+    lib = tre.load()
+    inp = workloads.make(args.workload)
+    T, d, E, k, I = inp.T, inp.d, inp.E, inp.k, inp.I
+    P = T * k
+    dev_dtype = torch.float32 if inp.dtype == "f32" else torch.bfloat16
+    dt = tre.MOE_F32 if inp.dtype == "f32" else tre.MOE_BF16
+
+    x = to_device(inp.x, torch)
+    wgu = to_device(inp.w_gate_up, torch)
+    wd = to_device(inp.w_down, torch)
+    if inp.logits is not None:
+        logits = to_device(inp.logits, torch)
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    else:
+        logits = None
+        topk_idx = to_device(inp.pair_expert.reshape(T, k), torch)
+        topk_w = to_device(inp.pair_w.reshape(T, k), torch)
+    x_perm = torch.empty((P, d), dtype=dev_dtype, device="cuda")
+    row_token = torch.empty(P, dtype=torch.int32, device="cuda")
+    pair_row = torch.empty(P, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    h = torch.empty((P, I), dtype=dev_dtype, device="cuda")
+    y_perm = torch.empty((P, d), dtype=dev_dtype, device="cuda")
+    out = torch.empty((T, d), dtype=dev_dtype, device="cuda")
+    pws_bytes = lib.moe_permute_workspace_size(T, k, E)
+    pws = torch.empty(max(pws_bytes, 1), dtype=torch.uint8, device="cuda")
+    fws_bytes = lib.moe_forward_workspace_size(T, d, E, k, I, dt)
+    fws = torch.empty(max(fws_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    # raw C-ABI calls with the pointers marshalled once
+    calls = {
+        "route": (lambda: lib.moe_route_topk(ptr(logits), T, E, k, ptr(topk_idx), ptr(topk_w), sp))
+        if logits is not None else (lambda: 0),
+        "permute": lambda: lib.moe_permute(ptr(x), dt, T, d, k, ptr(topk_idx), E, ptr(x_perm), ptr(row_token),
+                                           ptr(pair_row), ptr(offsets), ptr(pws), pws_bytes, sp),
+        "gate_up": lambda: lib.moe_gate_up_swiglu(ptr(x_perm), ptr(offsets), P, E, d, I, ptr(wgu), dt, ptr(h), sp),
+        "down": lambda: lib.moe_down_proj(ptr(h), ptr(offsets), P, E, d, I, ptr(wd), dt, ptr(y_perm), sp),
+        "combine": lambda: lib.moe_combine(ptr(y_perm), P, ptr(pair_row), ptr(topk_w), T, k, d, dt, ptr(out), sp),
+    }
+
+    def fused():
+        return lib.moe_forward(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(topk_idx),
+                               ptr(topk_w), None, None, None, ptr(out), ptr(fws), fws_bytes, sp)
+
+    def run_step(events=None):
+        for i, name in enumerate(STAGES):
+            if events is not None:
+                events[i].record(stream)
+            st = calls[name]()
+            if st != 0:
+                raise RuntimeError(f"{name} failed with status {st}")
+        if events is not None:
+            events[len(STAGES)].record(stream)
+
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    n_rows = int(offsets[E].item())
+    counts = (offsets[1:] - offsets[:-1]).cpu().numpy()
+    live = int((counts > 0).sum())
+
+    # ---- timed region: exactly K steps, events around every stage ----
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                for i, name in enumerate(STAGES)}
+    gpu_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][len(STAGES)]) for s in range(args.steps)]))
+
+    # the fused entry point, same kernels in one call
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    f0 = time.perf_counter()
+    for _ in range(args.steps):
+        if fused() != 0:
+            raise RuntimeError("moe_forward failed")
+    torch.cuda.synchronize()
+    fused_ms = (time.perf_counter() - f0) * 1e3 / args.steps
+
+    work = algorithmic_work(inp, n_rows, live)
+    peak_mm = PEAK_F32_TFLOPS if inp.dtype == "f32" else PEAK_BF16_TFLOPS
+    kernels = {}
+    for name in STAGES:
+        ms = stage_ms[name]
+        w = work[name]
+        ent = {"ms": round(ms, 5)}
+        if ms > 0 and w.get("bytes"):
+            ent["gbs"] = round(w["bytes"] / (ms * 1e-3) / 1e9, 1)
+            ent["hbm_frac"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+        if ms > 0 and w.get("flops"):
+            ent["tflops"] = round(w["flops"] / (ms * 1e-3) / 1e12, 1)
+            ent["mfma_frac"] = round(ent["tflops"] / peak_mm, 4)
+        kernels[name] = ent
+
+    gu = kernels["gate_up"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("source_sha256_16") == kernel_source_hash() and rec.get("workload") == args.workload:
+            traffic = rec.get("hbm_bytes_per_launch")
+    roofline = {
+        "bound": "mfma",
+        "kernel": "gate/up grouped GEMM + SwiGLU (k_grouped_gemm_bf16<true>)" if inp.dtype == "bf16"
+                  else "gate/up grouped FFN (k_ffn_gate_up_f32)",
+        "achieved": gu.get("tflops"),
+        "peak": peak_mm,
+        "unit": "TFLOP/s",
+        "frac": gu.get("mfma_frac"),
+        "traffic": traffic,
+        "flops_per_launch": work["gate_up"]["flops"],
+        "launch_ms": gu["ms"],
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": P / (ms_per_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "I": I, "pairs": P,
+                   "routed_rows": n_rows, "live_experts": live},
+        "roofline": roofline,
+        "kernels": kernels,
+        "gpu_ms_per_step": gpu_ms,
+        "fused_forward_ms_per_step": fused_ms,
+        "permute_gbs": kernels["permute"].get("gbs"),
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

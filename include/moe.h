@@ -21,8 +21,9 @@
  *    status is returned and nothing is enqueued.
  *  - Rows are row-major and dense (stride = row length).  Element type
  *    `moe_dtype`: MOE_F32 (IEEE float) or MOE_BF16 (bfloat16).
- *  - Limits: 1 <= k <= E <= 256; d and I multiples of 64; T*k*max(d, I) and
- *    every array size below 2^31 elements.  T == 0 is valid (nothing runs).
+ *  - Limits: 1 <= E <= 256; k >= 1, and k <= E where the call routes; d and
+ *    I multiples of 64; T*k*max(d, I) and every activation array below 2^31
+ *    elements.  T == 0 (or no rows) is valid: nothing is enqueued.
  *  - Device-side values that the host cannot see (expert ids, offsets, row
  *    indices) are clamped to the buffers they index: an expert id outside
  *    [0, E) drops its pair, a row index outside the capacity is skipped.
@@ -107,6 +108,19 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, in
                            int32_t E, int32_t d, int32_t I, const void* w_gate_up,
                            const void* w_down, moe_dtype dt, void* y_perm, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* The two halves of moe_grouped_ffn, for callers that schedule or time them
+ * separately.  Same operands, layouts and row ranges as moe_grouped_ffn:
+ *   moe_gate_up_swiglu:  h[r] = silu(x_perm[r] @ Wgu[e][:, :I]) * (x_perm[r] @ Wgu[e][:, I:])
+ *                        h [max_rows, I] dt (output)
+ *   moe_down_proj:       y_perm[r] = h[r] @ Wd[e]
+ * Neither needs a workspace.                                                  */
+moe_status moe_gate_up_swiglu(const void* x_perm, const int32_t* expert_offsets, int32_t max_rows,
+                              int32_t E, int32_t d, int32_t I, const void* w_gate_up, moe_dtype dt,
+                              void* h, void* stream);
+moe_status moe_down_proj(const void* h, const int32_t* expert_offsets, int32_t max_rows, int32_t E,
+                         int32_t d, int32_t I, const void* w_down, moe_dtype dt, void* y_perm,
+                         void* stream);
 
 /* ---- combine ----------------------------------------------------------------
  * "Expert parallelism", "Token dispatch" / "Adding an implementation": the

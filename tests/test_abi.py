@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {
         "moe_status_string", "moe_route_topk", "moe_permute_workspace_size", "moe_permute",
         "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
-        "moe_forward_workspace_size", "moe_forward"}
+        "moe_forward_workspace_size", "moe_forward", "moe_gate_up_swiglu", "moe_down_proj"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -94,3 +94,12 @@ def test_forward_validation(lib):
     assert f(*base[:2], 0, *base[3:]) == 0                           # T == 0
     # workspace grows with the batch
     assert lib.moe_forward_workspace_size(128, 128, 8, 2, 256, 0) > n
+
+
+def test_ffn_halves_validation(lib):
+    for f in (lib.moe_gate_up_swiglu, lib.moe_down_proj):
+        assert f(FAKE, FAKE, 100, 8, 128, 96, FAKE, 1, FAKE, None) == 2     # I % 64
+        assert f(FAKE, FAKE, 100, 0, 128, 128, FAKE, 1, FAKE, None) == 1    # E < 1
+        assert f(FAKE, FAKE, 100, 8, 128, 128, None, 1, FAKE, None) == 1    # NULL weight
+        assert f(FAKE, FAKE, 100, 8, 128, 128, FAKE, 5, FAKE, None) == 1    # bad dtype
+        assert f(None, None, 0, 8, 128, 128, None, 1, None, None) == 0      # no rows

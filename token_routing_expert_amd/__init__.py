@@ -10,6 +10,7 @@ Functions carry the C entry points' names:
   moe_route_topk    top-k + renormalised softmax routing
   moe_permute       pairs grouped by expert, token rows moved to expert order
   moe_grouped_ffn   each expert's SwiGLU feed-forward on its rows
+  moe_gate_up_swiglu / moe_down_proj   its two halves
   moe_combine       routing-weighted sum back to token order
   moe_forward       the whole layer
 """
@@ -63,6 +64,8 @@ def load(build_if_missing: bool = True):
         "moe_permute": ([p, st, i32, i32, i32, p, i32, p, p, p, p, p, sz, p], st),
         "moe_grouped_ffn_workspace_size": ([i32, i32, i32, i32, st], sz),
         "moe_grouped_ffn": ([p, p, i32, i32, i32, i32, p, p, st, p, p, sz, p], st),
+        "moe_gate_up_swiglu": ([p, p, i32, i32, i32, i32, p, st, p, p], st),
+        "moe_down_proj": ([p, p, i32, i32, i32, i32, p, st, p, p], st),
         "moe_combine": ([p, i32, p, p, i32, i32, i32, st, p, p], st),
         "moe_forward_workspace_size": ([i32, i32, i32, i32, i32, st], sz),
         "moe_forward": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, sz, p], st),
@@ -196,6 +199,37 @@ def moe_grouped_ffn(x_perm, expert_offsets, w_gate_up, w_down, y_perm=None, work
     _check("moe_grouped_ffn", lib.moe_grouped_ffn(_ptr(x_perm), _ptr(expert_offsets), R, E, d, I, _ptr(w_gate_up),
                                                   _ptr(w_down), dt, _ptr(y_perm), _ptr(ws), nbytes,
                                                   _stream(stream)))
+    return y_perm
+
+
+def moe_gate_up_swiglu(x_perm, expert_offsets, w_gate_up, h=None, stream=None):
+    """h[r] = silu(x_perm[r] @ Wgu[e][:, :I]) * (x_perm[r] @ Wgu[e][:, I:]) -> h [R, I]."""
+    torch = _torch()
+    lib = load()
+    R, d = x_perm.shape
+    E, d2, two_i = w_gate_up.shape
+    I = two_i // 2
+    _expect(w_gate_up, x_perm.dtype, (E, d, 2 * I), "w_gate_up")
+    _expect(expert_offsets, torch.int32, (E + 1,), "expert_offsets")
+    h = _empty((R, I), x_perm.dtype, x_perm) if h is None else h
+    _expect(h, x_perm.dtype, (R, I), "h")
+    _check("moe_gate_up_swiglu", lib.moe_gate_up_swiglu(_ptr(x_perm), _ptr(expert_offsets), R, E, d, I,
+                                                        _ptr(w_gate_up), _dt(x_perm), _ptr(h), _stream(stream)))
+    return h
+
+
+def moe_down_proj(h, expert_offsets, w_down, y_perm=None, stream=None):
+    """y_perm[r] = h[r] @ Wd[e] -> y_perm [R, d]."""
+    torch = _torch()
+    lib = load()
+    R, I = h.shape
+    E, I2, d = w_down.shape
+    _expect(w_down, h.dtype, (E, I, d), "w_down")
+    _expect(expert_offsets, torch.int32, (E + 1,), "expert_offsets")
+    y_perm = _empty((R, d), h.dtype, h) if y_perm is None else y_perm
+    _expect(y_perm, h.dtype, (R, d), "y_perm")
+    _check("moe_down_proj", lib.moe_down_proj(_ptr(h), _ptr(expert_offsets), R, E, d, I, _ptr(w_down), _dt(h),
+                                              _ptr(y_perm), _stream(stream)))
     return y_perm
 
 

@@ -132,6 +132,46 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, in
                                          (float*)y_perm, s));
 }
 
+namespace {
+
+moe_status check_ffn_half(const void* a, const int32_t* expert_offsets, int32_t max_rows, int32_t E, int32_t d,
+                          int32_t I, const void* w, moe_dtype dt, void* out) {
+  if (!dtype_ok(dt) || max_rows < 0) return MOE_ERR_ARG;
+  TRY(check_experts(E));
+  TRY(check_width(d));
+  TRY(check_width(I));
+  if ((int64_t)max_rows * (d > I ? d : I) >= kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)E * d * 2 * I >= 8 * kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if (max_rows > 0 && (!a || !expert_offsets || !w || !out)) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_gate_up_swiglu(const void* x_perm, const int32_t* expert_offsets, int32_t max_rows, int32_t E,
+                              int32_t d, int32_t I, const void* w_gate_up, moe_dtype dt, void* h, void* stream) {
+  TRY(check_ffn_half(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, dt, h));
+  if (max_rows == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == MOE_BF16)
+    return from_hip(launch_gate_up_bf16((const bf16_t*)x_perm, expert_offsets, max_rows, E, d, I,
+                                        (const bf16_t*)w_gate_up, (bf16_t*)h, s));
+  return from_hip(launch_gate_up_f32((const float*)x_perm, expert_offsets, max_rows, E, d, I,
+                                     (const float*)w_gate_up, (float*)h, s));
+}
+
+moe_status moe_down_proj(const void* h, const int32_t* expert_offsets, int32_t max_rows, int32_t E, int32_t d,
+                         int32_t I, const void* w_down, moe_dtype dt, void* y_perm, void* stream) {
+  TRY(check_ffn_half(h, expert_offsets, max_rows, E, d, I, w_down, dt, y_perm));
+  if (max_rows == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == MOE_BF16)
+    return from_hip(launch_down_bf16((const bf16_t*)h, expert_offsets, max_rows, E, d, I, (const bf16_t*)w_down,
+                                     (bf16_t*)y_perm, s));
+  return from_hip(launch_down_f32((const float*)h, expert_offsets, max_rows, E, d, I, (const float*)w_down,
+                                  (float*)y_perm, s));
+}
+
 moe_status moe_combine(const void* y_perm, int32_t max_rows, const int32_t* pair_row, const float* pair_w,
                        int32_t T, int32_t k, int32_t d, moe_dtype dt, void* out, void* stream) {
   if (!dtype_ok(dt) || T < 0 || k < 1 || max_rows < 0) return MOE_ERR_ARG;

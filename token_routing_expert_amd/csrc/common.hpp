@@ -51,7 +51,16 @@ hipError_t launch_move_rows(const void* x, int64_t T, int64_t row_bytes, const i
                             const int32_t* expert_offsets, int E, int64_t max_rows, void* x_perm,
                             hipStream_t s);
 
-// Grouped SwiGLU feed-forward.  h: [max_rows, I] scratch of the activation type.
+// Grouped SwiGLU feed-forward, as two launches (gate/up + SwiGLU, then down).
+// h: [max_rows, I] of the activation type.
+hipError_t launch_gate_up_bf16(const bf16_t* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
+                               int d, int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s);
+hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
+                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s);
+hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
+                              int d, int I, const float* w_gate_up, float* h, hipStream_t s);
+hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
+                           int I, const float* w_down, float* y_perm, hipStream_t s);
 hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets,
                                    int64_t max_rows, int E, int d, int I, const bf16_t* w_gate_up,
                                    const bf16_t* w_down, bf16_t* h, bf16_t* y_perm, hipStream_t s);
