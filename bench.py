@@ -37,7 +37,7 @@ METRIC = "routed token-expert pairs/sec per MoE layer; % bf16 MFMA peak; permute
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up.json")
+PROFILES = os.path.join(ROOT, "profiles")
 GEMM_SOURCE = os.path.join(ROOT, "token_routing_expert_amd", "csrc", "grouped_ffn.hip")
 STAGES = ["route", "permute", "gate_up", "down", "combine"]
 
@@ -45,6 +45,22 @@ STAGES = ["route", "permute", "gate_up", "down", "combine"]
 def kernel_source_hash() -> str:
     with open(GEMM_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic_record(workload: str):
+    """Key/value lines ('key: value') of the counter summary for the gate/up
+    kernel on this workload, or None.  The record carries the hash of the
+    kernel source it was measured on; a changed kernel has no traffic."""
+    path = os.path.join(PROFILES, f"gate_up_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        line = line.strip().lstrip("-* ")
+        if ":" in line:
+            k, v = line.split(":", 1)
+            rec[k.strip().strip("`")] = v.strip().strip("`")
+    return rec if "hbm_bytes_per_launch" in rec else None
 
 
 def to_device(a, torch):
@@ -185,14 +201,18 @@ def main() -> int:
             events[len(STAGES)].record(stream)
 
     if args.copy_calibration_mb > 0:
+        # a device-to-device copy of known size whose source is not cache
+        # resident (a 1 GiB write in between evicts the 256 MB Infinity Cache)
         n = args.copy_calibration_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         src.fill_(1)
+        flush.fill_(2)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, flush
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -241,13 +261,12 @@ def main() -> int:
 
     gu = kernels["gate_up"]
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("source_sha256_16") == kernel_source_hash() and rec.get("workload") == args.workload:
-            traffic = rec.get("hbm_bytes_per_launch")
+    rec = read_traffic_record(args.workload)
+    if rec is not None and rec.get("source_sha256_16") == kernel_source_hash():
+        traffic = float(rec["hbm_bytes_per_launch"])
     roofline = {
         "bound": "mfma",
-        "kernel": "gate/up grouped GEMM + SwiGLU (k_grouped_gemm_bf16<true>)" if inp.dtype == "bf16"
+        "kernel": "gate/up grouped GEMM + SwiGLU (dma::k_grouped_gemm<true, 32, 2>)" if inp.dtype == "bf16"
                   else "gate/up grouped FFN (k_ffn_gate_up_f32)",
         "achieved": gu.get("tflops"),
         "peak": peak_mm,

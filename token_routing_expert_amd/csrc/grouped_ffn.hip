@@ -9,26 +9,26 @@
 //   H[r] = silu(x_perm[r] @ Wgu[e][:, :I]) * (x_perm[r] @ Wgu[e][:, I:])
 //   Y[r] = H[r] @ Wd[e]
 //
-// bf16 path (MFMA, gfx950):
-//   * One kernel template, two instances: gate/up with the SwiGLU epilogue
-//     (output H, bf16) and down (output Y, bf16); float32 accumulation in
-//     v_mfma_f32_32x32x16_bf16.
-//   * Workgroup tile 128 rows x 256 weight columns x 64 k, 4 waves in 2 x 2,
-//     each wave 64 x 128 (2 x 4 MFMA tiles).  For gate/up the 256 columns
-//     are 128 gate columns and the matching 128 up columns, and every wave
-//     holds gate column j and up column j in the same lane, so the SwiGLU
-//     epilogue is elementwise in registers.
-//   * Activation tile [128][64] and weight tile [64][256] staged in LDS with
-//     padded rows; the next k-stage is prefetched into registers while the
-//     current one is multiplied.  Activation rows are k-contiguous and read
-//     with ds_read_b128; weight rows are n-contiguous and read with the
-//     gfx950 transposing ds_read_b64_tr_b16, two per operand.
-//   * Persistent grid: each workgroup derives the tile list from the device
-//     offsets (no host synchronisation), walks it round-robin, and tiles are
-//     ordered expert, then column tile, then row tile so that the row tiles
-//     sharing a weight slice run at the same time on one XCD's L2.
-// float32 path: plain per-element dot products (small, exact-ish, for the
-// float32 workloads).
+// bf16 path (MFMA, gfx950), one kernel template with two instances: gate/up
+// with the SwiGLU epilogue (output H) and down (output Y), both bf16 with
+// float32 accumulation in v_mfma_f32_32x32x16_bf16:
+//   * workgroup tile 128 rows x 256 weight columns, 4 waves in 2 x 2, each
+//     wave 64 x 128 (2 x 4 MFMA tiles); for gate/up the 256 columns are 128
+//     gate columns and the matching 128 up columns, and each wave holds gate
+//     column j and up column j in the same lane, so SwiGLU is elementwise in
+//     registers;
+//   * k-stages of 32 stream through a ring of three LDS buffers filled by
+//     buffer loads that write LDS directly; two workgroups per CU, so one
+//     workgroup's waits overlap the other's multiplications;
+//   * weight rows are n-contiguous and reach the MFMA through the gfx950
+//     transposing LDS read ds_read_b64_tr_b16;
+//   * persistent grid: each workgroup derives the tile list from the device
+//     offsets (no host synchronisation) and walks it round-robin; tiles are
+//     ordered expert, then column tile, then row tile, and consecutive tiles
+//     go to workgroups of one XCD, so the row tiles that share a weight slice
+//     run together on one L2.
+// float32 path: plain per-element dot products (small, for the float32
+// workloads).
 #include "common.hpp"
 
 namespace tre {
@@ -40,12 +40,6 @@ constexpr int kXcd = 8;          // XCDs per MI355X; workgroups are dealt round-
 // offsets that are always past num_records (a load there returns zeros).
 constexpr int kBufferConfig = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr uint32_t kStagePast = 0x40000000u;
-// LDS rows are padded: activation rows by 16 bytes (16 consecutive rows of a
-// ds_read_b128 land on distinct banks for 64- and 32-element rows), weight
-// rows by 64 bytes (the 4 consecutive k-rows of a ds_read_b64_tr_b16 group
-// land on distinct banks).
-
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -77,289 +71,19 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
   return before + x - v;
 }
 
-// Tile shape.  Four waves; wave tile WTM rows x 128 weight columns (MI x 4
-// MFMA 32x32 tiles, MI = WTM / 32); WM x WN waves per workgroup.
-template <int WTM_, int WM_, int BK_, bool SWIGLU_, int OCC_ = 1>
-struct Tile {
-  static constexpr int WTM = WTM_, WM = WM_, WN = 4 / WM_, BK = BK_;
-  static constexpr int OCC = OCC_;                       // workgroups per CU the launch aims for
-  static constexpr bool SWIGLU = SWIGLU_;
-  static constexpr int MI = WTM / 32;                    // MFMA row tiles per wave
-  static constexpr int BM = WTM * WM;                    // rows per workgroup tile
-  static constexpr int BNB = 128 * WN;                   // weight columns per tile
-  static constexpr int BNO = SWIGLU ? BNB / 2 : BNB;     // output columns per tile
-  static constexpr int A_LD = BK + 8;                    // padded LDS row (elements)
-  static constexpr int B_LD = BNB + 32;
-  static constexpr int A_STAGE = BM * A_LD;              // elements per LDS stage
-  static constexpr int B_STAGE = BK * B_LD;
-  static constexpr int A_CHUNKS = BM * BK / 8 / NTHR;    // 16-byte copies per thread per stage
-  static constexpr int B_CHUNKS = BK * BNB / 8 / NTHR;
-  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small for 256 threads");
-  static constexpr size_t LDS_BYTES = 2 * (A_STAGE + B_STAGE) * sizeof(bf16_t);
-};
-
-// A: [max_rows, K] activations; W: [E, K, ldw] weights; Out: [max_rows, N].
-// SWIGLU: N = I, ldw = 2I; the weight tile holds BNB/2 gate columns and the
-// matching BNB/2 up columns, output columns [n0, n0 + BNB/2).
-// plain:  N = d, ldw = d; output columns [n0, n0 + BNB).
-// The MFMA is issued with the weight fragment as its first operand, so the
-// accumulator is the transposed tile: each lane owns one output row and
-// groups of 4 consecutive output columns, stored 8 bytes at a time.
-template <class C>
-__global__ __launch_bounds__(NTHR, C::OCC) void k_grouped_gemm_bf16(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K,
-    int N, int ldw, const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2 * C::A_STAGE];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2 * C::B_STAGE];
-  __shared__ int s_start[kMaxExperts];
-  __shared__ int s_mt[kMaxExperts];
-  __shared__ int64_t s_lo[kMaxExperts];
-  __shared__ int s_cnt[kMaxExperts];
-  __shared__ int s_wave[NTHR / kWave];
-
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-
-  // ---- tile list from the device offsets ----
-  int mt = 0;
-  if (tid < E) {
-    const int64_t lo = clampi<int64_t>(offsets[tid], 0, max_rows);
-    const int64_t hi = clampi<int64_t>(offsets[tid + 1], lo, max_rows);
-    s_lo[tid] = lo;
-    s_cnt[tid] = (int)(hi - lo);
-    mt = (int)ceil_div(hi - lo, C::BM);
-    s_mt[tid] = mt;
-  }
-  int total_mt = 0;
-  const int start = block_exclusive_scan(mt, s_wave, &total_mt);
-  if (tid < E) s_start[tid] = start;
-  __syncthreads();
-  const int64_t total_tiles = (int64_t)total_mt * n_tiles;
-
-  // XCD-aware order: workgroups b, b+8, b+16 ... share an XCD; give them
-  // consecutive tiles.
-  const int G = gridDim.x;
-  const int vb = (blockIdx.x % kXcd) * (G / kXcd) + blockIdx.x / kXcd;
-
-  // per-thread constant parts of the global->LDS copies (16 B each)
-  constexpr int A_CPR = C::BK / 8;        // chunks per activation row
-  constexpr int B_CPR = C::BNB / 8;       // chunks per weight row
-  const int a_col = (tid % A_CPR) * 8, a_row0 = tid / A_CPR;
-  const int b_tcol = (tid % B_CPR) * 8, b_row0 = tid / B_CPR;
-  constexpr int A_RSTEP = NTHR / A_CPR, B_RSTEP = NTHR / B_CPR;
-
-  const int g = lane / 16, L = lane % 16;
-
-  for (int64_t v = vb; v < total_tiles; v += G) {
-    // expert: the last one whose first tile is <= v (empty experts own no tiles)
-    int lo_e = 0, hi_e = E - 1;
-    while (lo_e < hi_e) {
-      const int mid = (lo_e + hi_e + 1) / 2;
-      if ((int64_t)s_start[mid] * n_tiles <= v) lo_e = mid; else hi_e = mid - 1;
-    }
-    // every lane computed the same tile; make that visible to the compiler so
-    // the tile's addresses and buffer descriptors live in scalar registers
-    const int e = __builtin_amdgcn_readfirstlane(lo_e);
-    const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
-    const int e_mt = __builtin_amdgcn_readfirstlane(s_mt[e]);
-    const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
-    const int64_t e_lo = s_lo[e];
-    const int64_t e_row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(e_lo >> 32)) << 32) |
-                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)e_lo);
-    const int64_t local = v - (int64_t)e_start * n_tiles;
-    const int nt = (int)(local / e_mt);
-    const int mtile = (int)(local % e_mt);
-    const int64_t row0 = e_row0 + (int64_t)mtile * C::BM;
-    const int rows = min(C::BM, e_cnt - mtile * C::BM);
-    const int n0 = nt * C::BNO;
-    const bf16_t* Wb = W + (int64_t)e * K * ldw;
-
-    int b_gcol;
-    bool b_ok;
-    if (C::SWIGLU) {
-      const int hc = n0 + (b_tcol % (C::BNB / 2));
-      b_ok = hc < N;
-      b_gcol = (b_tcol < C::BNB / 2) ? hc : N + hc;
-    } else {
-      b_gcol = n0 + b_tcol;
-      b_ok = b_gcol < N;
-    }
-
-    // Buffer descriptors bound this tile's activation rows and this expert's
-    // weights: a load past num_records returns zeros without touching memory,
-    // so ragged rows, absent columns and the stages past the last need no
-    // branches (and the compiler can count outstanding loads exactly).
-    const __amdgpu_buffer_rsrc_t a_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(A + row0 * K), (short)0, rows * K * 2, kBufferConfig);
-    const __amdgpu_buffer_rsrc_t b_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, K * ldw * 2, kBufferConfig);
-    uint32_t a_off[C::A_CHUNKS], b_off[C::B_CHUNKS];
-#pragma unroll
-    for (int p = 0; p < C::A_CHUNKS; ++p) {
-      const int r = a_row0 + A_RSTEP * p;
-      a_off[p] = (r < rows) ? (uint32_t)(r * K + a_col) * 2u : kOutOfRange;
-    }
-#pragma unroll
-    for (int p = 0; p < C::B_CHUNKS; ++p) {
-      const int kr = b_row0 + B_RSTEP * p;
-      b_off[p] = b_ok ? (uint32_t)(kr * ldw + b_gcol) * 2u : kOutOfRange;
-    }
-    const int nk = K / C::BK;
-    constexpr int NR = C::A_CHUNKS + C::B_CHUNKS;
-    // stage s -> registers; stages past the last read nothing
-    auto gload = [&](int s, u32x4* R) {
-      const uint32_t ka = (s < nk) ? (uint32_t)s * C::BK * 2u : kStagePast;
-      const uint32_t kb = (s < nk) ? (uint32_t)s * C::BK * ldw * 2u : kStagePast;
-#pragma unroll
-      for (int p = 0; p < C::A_CHUNKS; ++p) R[p] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[p] + ka, 0, 0);
-#pragma unroll
-      for (int p = 0; p < C::B_CHUNKS; ++p)
-        R[C::A_CHUNKS + p] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[p] + kb, 0, 0);
-    };
-    auto lstore = [&](int buf, const u32x4* R) {
-      bf16_t* as = As + buf * C::A_STAGE;
-      bf16_t* bs = Bs + buf * C::B_STAGE;
-#pragma unroll
-      for (int p = 0; p < C::A_CHUNKS; ++p) *(u32x4*)&as[(a_row0 + A_RSTEP * p) * C::A_LD + a_col] = R[p];
-#pragma unroll
-      for (int p = 0; p < C::B_CHUNKS; ++p)
-        *(u32x4*)&bs[(b_row0 + B_RSTEP * p) * C::B_LD + b_tcol] = R[C::A_CHUNKS + p];
-    };
-
-    // tile column of this wave's MFMA column tile j
-    auto col_base = [&](int j) {
-      if (C::SWIGLU) return (j < 2) ? 64 * wn + 32 * j : C::BNB / 2 + 64 * wn + 32 * (j - 2);
-      return 128 * wn + 32 * j;
-    };
-
-    f32x16 acc[4][C::MI];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.f;
-
-    auto compute = [&](int buf) {
-      const bf16_t* as = As + buf * C::A_STAGE;
-      const bf16_t* bs = Bs + buf * C::B_STAGE;
-#pragma unroll
-      for (int ks = 0; ks < C::BK / 16; ++ks) {
-        bf16x8 a[C::MI], b[4];
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-          a[i] = *(const bf16x8*)&as[(C::WTM * wm + 32 * i + lane % 32) * C::A_LD + ks * 16 + (lane / 32) * 8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int krow = ks * 16 + (g / 2) * 8 + L / 4;
-          const int col = col_base(j) + (g % 2) * 16 + 4 * (L % 4);
-          b[j] = lds_read_b_operand(&bs[krow * C::B_LD + col], &bs[(krow + 4) * C::B_LD + col]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < C::MI; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
-      }
-    };
-
-    // Two stages in registers, two in LDS: stage s is loaded in iteration
-    // s - 2, written to LDS at the end of iteration s - 1 and multiplied in
-    // iteration s; one barrier per stage.
-    u32x4 R0[NR], R1[NR];
-    gload(0, R0);
-    gload(1, R1);
-    lstore(0, R0);
-    __syncthreads();
-    // (scheduling fences keep the compiler from sinking the loads of stage
-    // s + 2 below the multiplications they are meant to overlap)
-    for (int kt = 0;;) {
-      gload(kt + 2, R0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nk) lstore(1, R1);
-      __syncthreads();
-      if (++kt >= nk) break;
-      gload(kt + 2, R1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nk) lstore(0, R0);
-      __syncthreads();
-      if (++kt >= nk) break;
-    }
-
-    // ---- epilogue: acc[j][i] holds output rows C::WTM*wm + 32*i + lane%32,
-    // columns col_base(j) + 8*q4 + 4*(lane/32) + {0..3} in elements 4*q4.. ----
-    const int lr = lane % 32, lc = 4 * (lane / 32);
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-      const int r = C::WTM * wm + 32 * i + lr;
-      if (r >= rows) continue;
-      bf16_t* orow = Out + (row0 + r) * N;
-      if (C::SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int c = n0 + 64 * wn + 32 * j + 8 * q4 + lc;
-            if (c >= N) continue;
-            uint32_t packed[2];
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              float hv[2];
-#pragma unroll
-              for (int u = 0; u < 2; ++u) {
-                const float gt = acc[j][i][4 * q4 + 2 * h2 + u], up = acc[j + 2][i][4 * q4 + 2 * h2 + u];
-                hv[u] = gt / (1.f + __expf(-gt)) * up;
-              }
-              packed[h2] = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
-            }
-            *(uint2*)(orow + c) = make_uint2(packed[0], packed[1]);
-          }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int c = n0 + 128 * wn + 32 * j + 8 * q4 + lc;
-            if (c >= N) continue;
-            const uint32_t p0 = (uint32_t)f32_to_bf16(acc[j][i][4 * q4]) |
-                                ((uint32_t)f32_to_bf16(acc[j][i][4 * q4 + 1]) << 16);
-            const uint32_t p1 = (uint32_t)f32_to_bf16(acc[j][i][4 * q4 + 2]) |
-                                ((uint32_t)f32_to_bf16(acc[j][i][4 * q4 + 3]) << 16);
-            *(uint2*)(orow + c) = make_uint2(p0, p1);
-          }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// LDS-DMA pipeline (the bf16 path).  Workgroup tile 128 rows x 256 weight
-// columns x 64 k; 4 waves in 2 x 2, each 64 x 128 (2 x 4 MFMA 32x32 tiles).
-// Tiles stream through a ring of three LDS stages filled by buffer loads that
-// write LDS directly (no staging registers): while stage s is multiplied,
-// stages s+1 and s+2 are in flight.  One barrier per stage; each wave waits
-// for its own loads of the stage (vmcnt) before the barrier, so after the
-// barrier the whole stage is resident.
+// The bf16 grouped GEMM.  Tiles stream through a ring of three LDS stages
+// filled by buffer loads that write LDS directly (no staging registers):
+// while stage s is multiplied, stages s+1 and s+2 are in flight.  One
+// barrier per stage; each wave waits for its own loads of the stage (vmcnt)
+// before the barrier, so after the barrier the whole stage is resident.
 // LDS layouts are dense (a DMA instruction fills 1 KB contiguously) and
-// XOR-swizzled instead of padded:
-//   activation rows (64 k = 128 B = 8 chunks of 16 B): chunk c of row r sits
-//     in slot c ^ ((r >> 1) & 7), so a ds_read_b128 of 16 consecutive rows
-//     touches every bank once;
-//   weight rows (256 columns = 512 B = 32 chunks): chunk c of k-row kr sits
-//     in slot c ^ (4 * (kr & 3)), so the 4 consecutive k-rows x 32 bytes a
-//     16-lane ds_read_b64_tr_b16 group reads fall on distinct banks.
+// XOR-swizzled instead of padded, so that the activation reads
+// (ds_read_b128 of 16 consecutive rows) and the transposing weight reads (4
+// consecutive k-rows x 32 bytes per 16-lane group) touch every bank once.
 namespace dma {
 
-constexpr int BM = 128, BNB = 256, BK = 64;
-constexpr int A_BYTES = BM * BK * 2;           // 16 KB
-constexpr int B_BYTES = BK * BNB * 2;          // 32 KB
-constexpr int A_INSTR = A_BYTES / 1024 / 4;    // DMA instructions per wave per stage
-constexpr int B_INSTR = B_BYTES / 1024 / 4;
-constexpr int PER_STAGE = A_INSTR + B_INSTR;
+constexpr int BM = 128, BNB = 256;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -386,20 +110,42 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t a_slot_byte(int r, int c) { return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4)); }
-__device__ __forceinline__ uint32_t b_slot_byte(int kr, int c) { return (uint32_t)(kr * 512 + ((c ^ ((kr & 3) << 2)) << 4)); }
+// Stage geometry for k-depth BK (64 or 32).  Activation rows hold BK
+// elements (BK/8 chunks of 16 B); a DMA instruction fills 1 KB = RPI rows.
+template <int BK>
+struct Geo {
+  static constexpr int CPR = BK / 8;                     // 16-byte chunks per activation row
+  static constexpr int RPI = 1024 / (BK * 2);            // activation rows per DMA instruction
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BK * BNB * 2;           // 512-byte weight rows
+  static constexpr int A_INSTR = A_BYTES / 1024 / 4;     // per wave per stage
+  static constexpr int B_INSTR = B_BYTES / 1024 / 4;
+  static constexpr int PER_STAGE = A_INSTR + B_INSTR;
+  // chunk c of activation row r sits in slot c ^ swz(r): 16 consecutive rows
+  // read at one logical chunk land on 16 distinct bank groups
+  static __device__ __forceinline__ int swz(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
+  static __device__ __forceinline__ uint32_t a_byte(int r, int c) {
+    return (uint32_t)(r * (BK * 2) + ((c ^ swz(r)) << 4));
+  }
+};
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(NTHR, 1) void k_grouped_gemm(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                         int64_t max_rows, int E, int K, int N, int ldw,
-                                                         const bf16_t* __restrict__ W, bf16_t* __restrict__ Out,
-                                                         int n_tiles) {
-  __shared__ __attribute__((aligned(1024))) char sA0[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sA1[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sA2[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB0[B_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB1[B_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB2[B_BYTES];
+// chunk c of weight k-row kr sits in slot c ^ (4 * (kr & 3)): the 4
+// consecutive k-rows x 32 bytes read by a 16-lane ds_read_b64_tr_b16 group
+// fall on distinct banks
+__device__ __forceinline__ uint32_t b_byte(int kr, int c) { return (uint32_t)(kr * 512 + ((c ^ ((kr & 3) << 2)) << 4)); }
+
+template <bool SWIGLU, int BK, int OCC>
+__global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+                                                           int64_t max_rows, int E, int K, int N, int ldw,
+                                                           const bf16_t* __restrict__ W, bf16_t* __restrict__ Out,
+                                                           int n_tiles) {
+  typedef Geo<BK> GE;
+  __shared__ __attribute__((aligned(1024))) char sA0[GE::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sA1[GE::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sA2[GE::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB0[GE::B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB1[GE::B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB2[GE::B_BYTES];
   __shared__ int s_start[kMaxExperts];
   __shared__ int s_mt[kMaxExperts];
   __shared__ int64_t s_lo[kMaxExperts];
@@ -429,10 +175,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_grouped_gemm(const bf16_t* __restri
   const int G = gridDim.x;
   const int vb = (blockIdx.x % kXcd) * (G / kXcd) + blockIdx.x / kXcd;
 
-  // this lane's DMA slots: activation instruction p covers rows (wave + 4p) * 8 + lane / 8,
-  // weight instruction p covers k-rows (wave + 4p) * 2 + lane / 32
-  const int a_slot = lane % 8, b_slot = lane % 32;
-
   auto col_base = [&](int j) {
     if (SWIGLU) return (j < 2) ? 64 * wn + 32 * j : BNB / 2 + 64 * wn + 32 * (j - 2);
     return 128 * wn + 32 * j;
@@ -444,6 +186,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_grouped_gemm(const bf16_t* __restri
       const int mid = (lo_e + hi_e + 1) / 2;
       if ((int64_t)s_start[mid] * n_tiles <= v) lo_e = mid; else hi_e = mid - 1;
     }
+    // every lane found the same tile; say so, so that its addresses and
+    // buffer descriptors live in scalar registers
     const int e = __builtin_amdgcn_readfirstlane(lo_e);
     const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
     const int e_mt = __builtin_amdgcn_readfirstlane(s_mt[e]);
@@ -458,23 +202,28 @@ __global__ __launch_bounds__(NTHR, 1) void k_grouped_gemm(const bf16_t* __restri
     const int rows = min(BM, e_cnt - mtile * BM);
     const int n0 = nt * (SWIGLU ? BNB / 2 : BNB);
 
+    // Buffer descriptors bound this tile's activation rows and this expert's
+    // weights: a load past num_records returns zeros without touching memory.
     const __amdgpu_buffer_rsrc_t a_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(A + row0 * K), (short)0, rows * K * 2, kBufferConfig);
     const __amdgpu_buffer_rsrc_t b_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)e * K * ldw), (short)0, K * ldw * 2, kBufferConfig);
 
-    // byte offsets at k = 0 (out of range where the row or column does not exist)
-    uint32_t a_voff[A_INSTR], b_voff[B_INSTR];
+    // byte offsets at k = 0 (out of range where the row or column does not
+    // exist).  Activation instruction p of this wave fills rows
+    // (wave + 4p) * RPI + lane / CPR; weight instruction p fills k-rows
+    // (wave + 4p) * 2 + lane / 32.
+    uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
 #pragma unroll
-    for (int p = 0; p < A_INSTR; ++p) {
-      const int r = (wave + 4 * p) * 8 + lane / 8;
-      const int c = a_slot ^ ((r >> 1) & 7);
+    for (int p = 0; p < GE::A_INSTR; ++p) {
+      const int r = (wave + 4 * p) * GE::RPI + lane / GE::CPR;
+      const int c = (lane % GE::CPR) ^ GE::swz(r);
       a_voff[p] = (r < rows) ? (uint32_t)(r * K + c * 8) * 2u : kOutOfRange;
     }
 #pragma unroll
-    for (int p = 0; p < B_INSTR; ++p) {
+    for (int p = 0; p < GE::B_INSTR; ++p) {
       const int kr = (wave + 4 * p) * 2 + lane / 32;
-      const int c = b_slot ^ ((kr & 3) << 2);
+      const int c = (lane % 32) ^ ((kr & 3) << 2);
       const int tc = c * 8;
       int gcol;
       bool ok;
@@ -496,9 +245,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_grouped_gemm(const bf16_t* __restri
       const uint32_t a_lds = lds_address(a_buf) + wave * 1024;
       const uint32_t b_lds = lds_address(b_buf) + wave * 1024;
 #pragma unroll
-      for (int p = 0; p < A_INSTR; ++p) dma16(a_rsrc, a_lds + p * 4096, a_voff[p] + ka);
+      for (int p = 0; p < GE::A_INSTR; ++p) dma16(a_rsrc, a_lds + p * 4096, a_voff[p] + ka);
 #pragma unroll
-      for (int p = 0; p < B_INSTR; ++p) dma16(b_rsrc, b_lds + p * 4096, b_voff[p] + kb);
+      for (int p = 0; p < GE::B_INSTR; ++p) dma16(b_rsrc, b_lds + p * 4096, b_voff[p] + kb);
     };
 
     f32x16 acc[4][2];
@@ -516,13 +265,13 @@ __global__ __launch_bounds__(NTHR, 1) void k_grouped_gemm(const bf16_t* __restri
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int r = 64 * wm + 32 * i + lane % 32;
-          a[i] = *(const bf16x8*)(a_buf + a_slot_byte(r, ks * 2 + lane / 32));
+          a[i] = *(const bf16x8*)(a_buf + GE::a_byte(r, ks * 2 + lane / 32));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kr = ks * 16 + (g / 2) * 8 + L / 4;
           const int col = col_base(j) + (g % 2) * 16 + 4 * (L % 4);
-          const uint32_t off = b_slot_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
+          const uint32_t off = b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
           b[j] = lds_read_b_operand((const bf16_t*)(b_buf + off), (const bf16_t*)(b_buf + off + 4 * 512));
         }
 #pragma unroll
@@ -533,10 +282,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_grouped_gemm(const bf16_t* __restri
       }
     };
 
-    // stage kt lives in buffer kt % 3; stage kt + 2 is issued once every wave
-    // is past stage kt - 1 (the barrier), into the buffer stage kt - 1 used.
+    // Stage kt lives in buffer kt % 3.  At step kt each wave waits for its
+    // own loads of stage kt, the barrier makes the whole stage visible and
+    // guarantees every wave is done with stage kt - 1, whose buffer then
+    // receives stage kt + 2.
     auto step = [&](int kt, const char* a_cur, const char* b_cur, char* a_nxt, char* b_nxt) {
-      if (kt + 1 < nk) wait_vmcnt<PER_STAGE>(); else wait_vmcnt<0>();
+      if (kt + 1 < nk) wait_vmcnt<GE::PER_STAGE>(); else wait_vmcnt<0>();
       compiler_fence();
       __builtin_amdgcn_s_barrier();
       compiler_fence();
@@ -676,26 +427,12 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float* __restrict__ 
   y[r * d + c] = acc;
 }
 
-// Tile shapes: activation rows per workgroup tile (BM) against the rows an
-// expert is expected to hold.  Chosen on the host from sizes alone.
-typedef Tile<64, 2, 64, true> GateUpM128;     // BM 128, 128 gate + 128 up columns
-typedef Tile<64, 2, 64, false> DownM128;      // BM 128, 256 output columns
-
-template <class C>
-hipError_t launch_gemm(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
-                       const bf16_t* w, bf16_t* out, hipStream_t s) {
-  const int nt = (int)ceil_div(N, C::BNO);
-  k_grouped_gemm_bf16<C><<<persistent_grid(max_rows, E, C::BM, nt, C::OCC), NTHR, 0, s>>>(a, offsets, max_rows, E, K, N,
-                                                                                  ldw, w, out, nt);
-  return hipGetLastError();
-}
-
-template <bool SWIGLU>
+template <bool SWIGLU, int BK = 32, int OCC = 2>
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                       const bf16_t* w, bf16_t* out, hipStream_t s) {
   const int nt = (int)ceil_div(N, SWIGLU ? dma::BNB / 2 : dma::BNB);
-  dma::k_grouped_gemm<SWIGLU><<<persistent_grid(max_rows, E, dma::BM, nt, 1), NTHR, 0, s>>>(a, offsets, max_rows, E, K, N,
-                                                                                          ldw, w, out, nt);
+  dma::k_grouped_gemm<SWIGLU, BK, OCC><<<persistent_grid(max_rows, E, dma::BM, nt, OCC), NTHR, 0, s>>>(
+      a, offsets, max_rows, E, K, N, ldw, w, out, nt);
   return hipGetLastError();
 }
 
