@@ -23,7 +23,8 @@
  *    `moe_dtype`: MOE_F32 (IEEE float) or MOE_BF16 (bfloat16).
  *  - Limits: 1 <= E <= 256; k >= 1, and k <= E where the call routes; d and
  *    I multiples of 64; T*k*max(d, I) and every activation array below 2^31
- *    elements.  T == 0 (or no rows) is valid: nothing is enqueued.
+ *    elements; one expert's weights (4*d*I bytes for gate/up) below 2 GiB.
+ *    T == 0 (or no rows) is valid: nothing is enqueued.
  *  - Device-side values that the host cannot see (expert ids, offsets, row
  *    indices) are clamped to the buffers they index: an expert id outside
  *    [0, E) drops its pair, a row index outside the capacity is skipped.
@@ -78,7 +79,9 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
  * expert e owns rows [expert_offsets[e], expert_offsets[e+1]).
  *   x               [T, d] dt
  *   pair_expert     [T*k] int32
- *   x_perm          [T*k, d] dt   (output; rows >= expert_offsets[E] untouched)
+ *   x_perm          [T*k, d] dt   (output; rows >= expert_offsets[E] untouched;
+ *                   NULL: only the index arrays are built, no rows move, and
+ *                   x may be NULL too)
  *   row_token       [T*k] int32   (output; row r holds token row_token[r])
  *   pair_row        [T*k] int32   (output; row of pair p, -1 when dropped)
  *   expert_offsets  [E+1] int32   (output)
@@ -111,13 +114,18 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, in
 
 /* The two halves of moe_grouped_ffn, for callers that schedule or time them
  * separately.  Same operands, layouts and row ranges as moe_grouped_ffn:
- *   moe_gate_up_swiglu:  h[r] = silu(x_perm[r] @ Wgu[e][:, :I]) * (x_perm[r] @ Wgu[e][:, I:])
+ *   moe_gate_up_swiglu:  h[r] = silu(a_r @ Wgu[e][:, :I]) * (a_r @ Wgu[e][:, I:])
  *                        h [max_rows, I] dt (output)
+ *     row_token == NULL: a_r = x[r], x is the expert-ordered x_perm [max_rows, d];
+ *     row_token != NULL: a_r = x[row_token[r]], x is the token batch [x_rows, d]
+ *       (the row move of moe_permute done inside the projection's loads;
+ *       bf16 only, and x_rows * d below 2^30; row_token as moe_permute
+ *       writes it).
  *   moe_down_proj:       y_perm[r] = h[r] @ Wd[e]
  * Neither needs a workspace.                                                  */
-moe_status moe_gate_up_swiglu(const void* x_perm, const int32_t* expert_offsets, int32_t max_rows,
+moe_status moe_gate_up_swiglu(const void* x, const int32_t* expert_offsets, int32_t max_rows,
                               int32_t E, int32_t d, int32_t I, const void* w_gate_up, moe_dtype dt,
-                              void* h, void* stream);
+                              const int32_t* row_token, int32_t x_rows, void* h, void* stream);
 moe_status moe_down_proj(const void* h, const int32_t* expert_offsets, int32_t max_rows, int32_t E,
                          int32_t d, int32_t I, const void* w_down, moe_dtype dt, void* y_perm,
                          void* stream);

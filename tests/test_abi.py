@@ -56,6 +56,7 @@ def test_permute_validation(lib):
     assert f(*args[:1], 7, *args[2:]) == 1                           # bad dtype
     assert f(*args[:12], ws - 1, None) == 3                          # small workspace
     assert f(*args[:5], None, *args[6:]) == 1                        # NULL pair_expert
+    assert f(None, *args[1:]) == 1                                   # rows to move but no x
     assert f(FAKE, 1, 0, 128, 2, None, 16, None, None, None, FAKE, None, 0, None) == 0   # T == 0
 
 
@@ -97,9 +98,22 @@ def test_forward_validation(lib):
 
 
 def test_ffn_halves_validation(lib):
-    for f in (lib.moe_gate_up_swiglu, lib.moe_down_proj):
-        assert f(FAKE, FAKE, 100, 8, 128, 96, FAKE, 1, FAKE, None) == 2     # I % 64
-        assert f(FAKE, FAKE, 100, 0, 128, 128, FAKE, 1, FAKE, None) == 1    # E < 1
-        assert f(FAKE, FAKE, 100, 8, 128, 128, None, 1, FAKE, None) == 1    # NULL weight
-        assert f(FAKE, FAKE, 100, 8, 128, 128, FAKE, 5, FAKE, None) == 1    # bad dtype
-        assert f(None, None, 0, 8, 128, 128, None, 1, None, None) == 0      # no rows
+    f = lib.moe_down_proj
+    assert f(FAKE, FAKE, 100, 8, 128, 96, FAKE, 1, FAKE, None) == 2     # I % 64
+    assert f(FAKE, FAKE, 100, 0, 128, 128, FAKE, 1, FAKE, None) == 1    # E < 1
+    assert f(FAKE, FAKE, 100, 8, 128, 128, None, 1, FAKE, None) == 1    # NULL weight
+    assert f(FAKE, FAKE, 100, 8, 128, 128, FAKE, 5, FAKE, None) == 1    # bad dtype
+    assert f(None, None, 0, 8, 128, 128, None, 1, None, None) == 0      # no rows
+    g = lib.moe_gate_up_swiglu
+    assert g(FAKE, FAKE, 100, 8, 128, 96, FAKE, 1, None, 0, FAKE, None) == 2       # I % 64
+    assert g(FAKE, FAKE, 100, 0, 128, 128, FAKE, 1, None, 0, FAKE, None) == 1      # E < 1
+    assert g(FAKE, FAKE, 100, 8, 128, 128, None, 1, None, 0, FAKE, None) == 1      # NULL weight
+    assert g(FAKE, FAKE, 100, 8, 128, 128, FAKE, 0, FAKE, 50, FAKE, None) == 2     # gather is bf16 only
+    assert g(FAKE, FAKE, 100, 8, 128, 128, FAKE, 1, FAKE, -1, FAKE, None) == 1     # x_rows < 0
+    assert g(FAKE, FAKE, 100, 8, 1024, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None) == 2  # x too large for gathering
+    assert g(None, None, 0, 8, 128, 128, None, 1, None, 0, None, None) == 0        # no rows
+
+
+def test_weight_size_limit(lib):
+    # one expert's gate/up weight 4*d*I bytes must stay below 2 GiB
+    assert lib.moe_down_proj(FAKE, FAKE, 100, 2, 32768, 16384, FAKE, 1, FAKE, None) == 2

@@ -203,6 +203,37 @@ def test_grouped_ffn_empty_experts(tre):
     check_grouped_ffn(tre, inp, idx)
 
 
+@pytest.mark.parametrize("T,d,E,k,I", [(300, 256, 5, 2, 320), (1500, 128, 3, 2, 256)])
+def test_gate_up_reads_token_rows_in_place(tre, T, d, E, k, I):
+    # index-only permutation + the projection reading x[row_token[r]] gives the
+    # same h, bit for bit, as moving the rows first
+    torch = _torch()
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + 1, logits="normal_bias")
+    idx, _ = oracle.route(inp.logits, k)
+    xd, pe = to_device(inp.x), to_device(idx.reshape(-1))
+    wgu = to_device(inp.w_gate_up)
+    x_perm, row_token, pair_row, offsets = tre.moe_permute(xd, pe, k, E)
+    _, row_token2, pair_row2, offsets2 = tre.moe_permute(xd, pe, k, E, move_rows=False)
+    sync()
+    assert torch.equal(row_token[: int(offsets[-1])], row_token2[: int(offsets2[-1])])
+    assert torch.equal(offsets, offsets2) and torch.equal(pair_row, pair_row2)
+    h1 = tre.moe_gate_up_swiglu(x_perm, offsets, wgu)
+    h2 = tre.moe_gate_up_swiglu(xd, offsets, wgu, row_token=row_token2, max_rows=T * k)
+    sync()
+    n = int(offsets[-1])
+    assert torch.equal(h1[:n].view(torch.int16), h2[:n].view(torch.int16))
+    # and against the oracle's h, through the down projection's input
+    y = tre.moe_down_proj(h2, offsets, to_device(inp.w_down))
+    sync()
+    _, y_pair = oracle.moe_tokens(inp.x, idx, np.ones(idx.shape), inp.w_gate_up, inp.w_down, want_y=True)
+    pr = oracle.dispatch(idx.reshape(-1), k, E)[1].reshape(T, k)
+    ref = np.zeros((n, d))
+    for t in range(T):
+        for j in range(k):
+            ref[pr[t, j]] = y_pair[t, j]
+    assert rel_l2(to_host(y)[:n], ref) <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("T,k,d,dtype", [(1000, 4, 256, "bf16"), (333, 2, 64, "f32"), (50, 8, 2880, "bf16")])

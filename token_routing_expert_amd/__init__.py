@@ -64,7 +64,7 @@ def load(build_if_missing: bool = True):
         "moe_permute": ([p, st, i32, i32, i32, p, i32, p, p, p, p, p, sz, p], st),
         "moe_grouped_ffn_workspace_size": ([i32, i32, i32, i32, st], sz),
         "moe_grouped_ffn": ([p, p, i32, i32, i32, i32, p, p, st, p, p, sz, p], st),
-        "moe_gate_up_swiglu": ([p, p, i32, i32, i32, i32, p, st, p, p], st),
+        "moe_gate_up_swiglu": ([p, p, i32, i32, i32, i32, p, st, p, i32, p, p], st),
         "moe_down_proj": ([p, p, i32, i32, i32, i32, p, st, p, p], st),
         "moe_combine": ([p, i32, p, p, i32, i32, i32, st, p, p], st),
         "moe_forward_workspace_size": ([i32, i32, i32, i32, i32, st], sz),
@@ -152,22 +152,27 @@ def moe_route_topk(logits, k: int, topk_idx=None, topk_w=None, stream=None):
 
 
 def moe_permute(x, pair_expert, k: int, E: int, x_perm=None, row_token=None, pair_row=None,
-                expert_offsets=None, workspace=None, stream=None):
+                expert_offsets=None, workspace=None, stream=None, move_rows: bool = True):
     """Group pairs by expert and move token rows.
 
     x [T, d]; pair_expert [T*k] (or [T, k]) int32 -> (x_perm [T*k, d], row_token [T*k],
-    pair_row [T*k], expert_offsets [E+1])."""
+    pair_row [T*k], expert_offsets [E+1]).  With ``move_rows=False`` only the index
+    arrays are built and x_perm is None."""
     torch = _torch()
     lib = load()
     T, d = x.shape
     P = T * k
     pe = pair_expert.reshape(-1)
     _expect(pe, torch.int32, (P,), "pair_expert")
-    x_perm = _empty((P, d), x.dtype, x) if x_perm is None else x_perm
+    if not move_rows:
+        x_perm = None
+    elif x_perm is None:
+        x_perm = _empty((P, d), x.dtype, x)
     row_token = _empty((P,), torch.int32, x) if row_token is None else row_token
     pair_row = _empty((P,), torch.int32, x) if pair_row is None else pair_row
     expert_offsets = _empty((E + 1,), torch.int32, x) if expert_offsets is None else expert_offsets
-    _expect(x_perm, x.dtype, (P, d), "x_perm")
+    if x_perm is not None:
+        _expect(x_perm, x.dtype, (P, d), "x_perm")
     _expect(row_token, torch.int32, (P,), "row_token")
     _expect(pair_row, torch.int32, (P,), "pair_row")
     _expect(expert_offsets, torch.int32, (E + 1,), "expert_offsets")
@@ -202,19 +207,30 @@ def moe_grouped_ffn(x_perm, expert_offsets, w_gate_up, w_down, y_perm=None, work
     return y_perm
 
 
-def moe_gate_up_swiglu(x_perm, expert_offsets, w_gate_up, h=None, stream=None):
-    """h[r] = silu(x_perm[r] @ Wgu[e][:, :I]) * (x_perm[r] @ Wgu[e][:, I:]) -> h [R, I]."""
+def moe_gate_up_swiglu(x, expert_offsets, w_gate_up, h=None, row_token=None, max_rows=None, stream=None):
+    """h[r] = silu(a_r @ Wgu[e][:, :I]) * (a_r @ Wgu[e][:, I:]) -> h [R, I].
+
+    Without ``row_token``, ``x`` is the expert-ordered x_perm [R, d] and a_r = x[r].
+    With ``row_token`` [R] (as moe_permute writes it), ``x`` is the token batch and
+    a_r = x[row_token[r]]; R = ``max_rows`` (default len(row_token))."""
     torch = _torch()
     lib = load()
-    R, d = x_perm.shape
+    x_rows, d = x.shape
+    if row_token is None:
+        R = x_rows
+    else:
+        R = int(max_rows if max_rows is not None else row_token.shape[0])
+        _expect(row_token, torch.int32, (row_token.shape[0],), "row_token")
+        if row_token.shape[0] < R:
+            raise ValueError("row_token holds fewer rows than max_rows")
     E, d2, two_i = w_gate_up.shape
     I = two_i // 2
-    _expect(w_gate_up, x_perm.dtype, (E, d, 2 * I), "w_gate_up")
+    _expect(w_gate_up, x.dtype, (E, d, 2 * I), "w_gate_up")
     _expect(expert_offsets, torch.int32, (E + 1,), "expert_offsets")
-    h = _empty((R, I), x_perm.dtype, x_perm) if h is None else h
-    _expect(h, x_perm.dtype, (R, I), "h")
-    _check("moe_gate_up_swiglu", lib.moe_gate_up_swiglu(_ptr(x_perm), _ptr(expert_offsets), R, E, d, I,
-                                                        _ptr(w_gate_up), _dt(x_perm), _ptr(h), _stream(stream)))
+    h = _empty((R, I), x.dtype, x) if h is None else h
+    _expect(h, x.dtype, (R, I), "h")
+    _check("moe_gate_up_swiglu", lib.moe_gate_up_swiglu(_ptr(x), _ptr(expert_offsets), R, E, d, I, _ptr(w_gate_up),
+                                                        _dt(x), _ptr(row_token), x_rows, _ptr(h), _stream(stream)))
     return h
 
 

@@ -47,7 +47,7 @@ ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
   L.pair_row = o;  o += align256(P * 4);
   L.row_token = o; o += align256(P * 4);
   L.offsets = o;   o += align256((E + 1) * 4);
-  L.x_perm = o;    o += align256(P * d * s);
+  L.x_perm = o;    o += dt == MOE_F32 ? align256(P * d * s) : 0;   // bf16 gathers rows in place
   L.h = o;         o += align256(P * I * s);
   L.y_perm = o;    o += align256(P * d * s);
   L.perm_ws = o;   o += permute_index_workspace(P, (int)E);
@@ -95,11 +95,12 @@ moe_status moe_permute(const void* x, moe_dtype dt, int32_t T, int32_t d, int32_
   const int64_t P = (int64_t)T * k;
   if (P * d >= kMaxElems) return MOE_ERR_UNSUPPORTED;
   if (!expert_offsets) return MOE_ERR_ARG;
-  if (T > 0 && (!x || !pair_expert || !x_perm || !row_token || !pair_row)) return MOE_ERR_ARG;
+  if (T > 0 && (!pair_expert || !row_token || !pair_row || (x_perm && !x))) return MOE_ERR_ARG;
   if (workspace_bytes < moe_permute_workspace_size(T, k, E) || (T > 0 && !workspace)) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   TRY(from_hip(launch_permute_index(pair_expert, P, k, E, row_token, pair_row, expert_offsets, workspace, s)));
+  if (!x_perm) return MOE_OK;   // index only: the caller gathers rows itself
   return from_hip(launch_move_rows(x, T, (int64_t)d * elem_size(dt), row_token, expert_offsets, E, P, x_perm, s));
 }
 
@@ -119,6 +120,7 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, in
   TRY(check_width(I));
   if ((int64_t)max_rows * (d > I ? d : I) >= kMaxElems) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)E * d * 2 * I >= 8 * kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d * I * 4 >= kMaxElems) return MOE_ERR_UNSUPPORTED;   // one expert's weights < 2 GiB
   if (max_rows == 0) return MOE_OK;
   if (!x_perm || !expert_offsets || !w_gate_up || !w_down || !y_perm) return MOE_ERR_ARG;
   if (!workspace || workspace_bytes < moe_grouped_ffn_workspace_size(max_rows, E, d, I, dt)) return MOE_ERR_WORKSPACE;
@@ -142,21 +144,28 @@ moe_status check_ffn_half(const void* a, const int32_t* expert_offsets, int32_t 
   TRY(check_width(I));
   if ((int64_t)max_rows * (d > I ? d : I) >= kMaxElems) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)E * d * 2 * I >= 8 * kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d * I * 4 >= kMaxElems) return MOE_ERR_UNSUPPORTED;   // one expert's weights < 2 GiB
   if (max_rows > 0 && (!a || !expert_offsets || !w || !out)) return MOE_ERR_ARG;
   return MOE_OK;
 }
 
 }  // namespace
 
-moe_status moe_gate_up_swiglu(const void* x_perm, const int32_t* expert_offsets, int32_t max_rows, int32_t E,
-                              int32_t d, int32_t I, const void* w_gate_up, moe_dtype dt, void* h, void* stream) {
-  TRY(check_ffn_half(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, dt, h));
+moe_status moe_gate_up_swiglu(const void* x, const int32_t* expert_offsets, int32_t max_rows, int32_t E,
+                              int32_t d, int32_t I, const void* w_gate_up, moe_dtype dt, const int32_t* row_token,
+                              int32_t x_rows, void* h, void* stream) {
+  TRY(check_ffn_half(x, expert_offsets, max_rows, E, d, I, w_gate_up, dt, h));
+  if (row_token) {
+    if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (x_rows < 0) return MOE_ERR_ARG;
+    if ((int64_t)x_rows * d >= kMaxElems / 2) return MOE_ERR_UNSUPPORTED;
+  }
   if (max_rows == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   if (dt == MOE_BF16)
-    return from_hip(launch_gate_up_bf16((const bf16_t*)x_perm, expert_offsets, max_rows, E, d, I,
-                                        (const bf16_t*)w_gate_up, (bf16_t*)h, s));
-  return from_hip(launch_gate_up_f32((const float*)x_perm, expert_offsets, max_rows, E, d, I,
+    return from_hip(launch_gate_up_bf16((const bf16_t*)x, expert_offsets, max_rows, E, d, I,
+                                        (const bf16_t*)w_gate_up, (bf16_t*)h, s, row_token, x_rows));
+  return from_hip(launch_gate_up_f32((const float*)x, expert_offsets, max_rows, E, d, I,
                                      (const float*)w_gate_up, (float*)h, s));
 }
 
@@ -202,6 +211,8 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
   const int64_t P = (int64_t)T * k;
   if (P * (d > I ? d : I) >= kMaxElems || (int64_t)T * E >= kMaxElems) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)E * d * 2 * I >= 8 * kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d * I * 4 >= kMaxElems) return MOE_ERR_UNSUPPORTED;   // one expert's weights < 2 GiB
+  if ((int64_t)T * d >= kMaxElems / 2) return MOE_ERR_UNSUPPORTED;   // x is addressed with 32-bit byte offsets
   if (T == 0) return MOE_OK;
   if (!x || !w_gate_up || !w_down || !topk_idx || !topk_w || !out) return MOE_ERR_ARG;
   const ForwardLayout L = forward_layout(T, d, E, k, I, dt);
@@ -218,12 +229,15 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
 
   if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
   TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s)));
-  TRY(from_hip(launch_move_rows(x, T, (int64_t)d * elem_size(dt), r_tok, offs, E, P, x_perm, s)));
   if (dt == MOE_BF16) {
-    TRY(from_hip(launch_grouped_ffn_bf16((const bf16_t*)x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up,
-                                         (const bf16_t*)w_down, (bf16_t*)h, (bf16_t*)y_perm, s)));
+    // the gate/up projection reads the token rows in place through row_token
+    // (no expert-ordered copy of x is materialised)
+    TRY(from_hip(launch_gate_up_bf16((const bf16_t*)x, offs, P, E, d, I, (const bf16_t*)w_gate_up, (bf16_t*)h, s,
+                                     r_tok, T)));
+    TRY(from_hip(launch_down_bf16((const bf16_t*)h, offs, P, E, d, I, (const bf16_t*)w_down, (bf16_t*)y_perm, s)));
     return from_hip(launch_combine_bf16((const bf16_t*)y_perm, P, p_row, topk_w, T, k, d, (bf16_t*)out, s));
   }
+  TRY(from_hip(launch_move_rows(x, T, (int64_t)d * elem_size(dt), r_tok, offs, E, P, x_perm, s)));
   TRY(from_hip(launch_grouped_ffn_f32((const float*)x_perm, offs, P, E, d, I, (const float*)w_gate_up,
                                       (const float*)w_down, (float*)h, (float*)y_perm, s)));
   return from_hip(launch_combine_f32((const float*)y_perm, P, p_row, topk_w, T, k, d, (float*)out, s));

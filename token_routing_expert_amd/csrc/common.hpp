@@ -53,8 +53,11 @@ hipError_t launch_move_rows(const void* x, int64_t T, int64_t row_bytes, const i
 
 // Grouped SwiGLU feed-forward, as two launches (gate/up + SwiGLU, then down).
 // h: [max_rows, I] of the activation type.
-hipError_t launch_gate_up_bf16(const bf16_t* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
-                               int d, int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s);
+// With row_token, activation row r is row row_token[r] of x ([x_rows, d]):
+// the permutation's row move happens inside the load.  Without, x is x_perm.
+hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
+                               int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s,
+                               const int32_t* row_token = nullptr, int64_t x_rows = 0);
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s);
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,

@@ -50,6 +50,7 @@ __device__ __forceinline__ bf16x8 lds_read_b_operand(const bf16_t* p0, const bf1
   return __builtin_bit_cast(bf16x8, v);
 }
 
+template <int NWAVES>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   int x = v;
@@ -62,7 +63,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < NTHR / kWave; ++w) {
+  for (int w = 0; w < NWAVES; ++w) {
     before += (w < wave) ? s_wave[w] : 0;
     all += s_wave[w];
   }
@@ -83,7 +84,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
 // consecutive k-rows x 32 bytes per 16-lane group) touch every bank once.
 namespace dma {
 
-constexpr int BM = 128, BNB = 256;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -110,16 +110,24 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Stage geometry for k-depth BK (64 or 32).  Activation rows hold BK
-// elements (BK/8 chunks of 16 B); a DMA instruction fills 1 KB = RPI rows.
-template <int BK>
+// Stage geometry for k-depth BK (64 or 32) and NJ MFMA column tiles per
+// wave (BNB = 64 NJ weight columns per workgroup tile).  Activation rows hold
+// BK elements (BK/8 chunks of 16 B); a DMA instruction fills 1 KB = RPI
+// activation rows or BRPI weight rows.
+template <int BK, int NJ, int WM>
 struct Geo {
+  static constexpr int WAVES = 2 * WM;                   // WM x 2 waves, each 64 rows x 32 NJ columns
+  static constexpr int BM = 64 * WM;                     // rows per workgroup tile
+  static constexpr int BNB = 64 * NJ;                    // weight columns per tile
+  static constexpr int BROW = BNB * 2;                   // bytes per weight row in LDS
+  static constexpr int BCPR = BROW / 16;                 // 16-byte chunks per weight row
+  static constexpr int BRPI = 1024 / BROW;               // weight rows per DMA instruction
   static constexpr int CPR = BK / 8;                     // 16-byte chunks per activation row
   static constexpr int RPI = 1024 / (BK * 2);            // activation rows per DMA instruction
   static constexpr int A_BYTES = BM * BK * 2;
-  static constexpr int B_BYTES = BK * BNB * 2;           // 512-byte weight rows
-  static constexpr int A_INSTR = A_BYTES / 1024 / 4;     // per wave per stage
-  static constexpr int B_INSTR = B_BYTES / 1024 / 4;
+  static constexpr int B_BYTES = BK * BROW;
+  static constexpr int A_INSTR = A_BYTES / 1024 / WAVES;  // per wave per stage
+  static constexpr int B_INSTR = B_BYTES / 1024 / WAVES;
   static constexpr int PER_STAGE = A_INSTR + B_INSTR;
   // chunk c of activation row r sits in slot c ^ swz(r): 16 consecutive rows
   // read at one logical chunk land on 16 distinct bank groups
@@ -127,19 +135,24 @@ struct Geo {
   static __device__ __forceinline__ uint32_t a_byte(int r, int c) {
     return (uint32_t)(r * (BK * 2) + ((c ^ swz(r)) << 4));
   }
+  // chunk c of weight k-row kr sits in slot c ^ (4 * (kr & 3)): the 4
+  // consecutive k-rows x 32 bytes read by a 16-lane ds_read_b64_tr_b16 group
+  // (and the neighbouring group's next 32 bytes) fall on distinct banks
+  static __device__ __forceinline__ uint32_t b_byte(int kr, int c) {
+    return (uint32_t)(kr * BROW + ((c ^ ((kr & 3) << 2)) << 4));
+  }
 };
 
-// chunk c of weight k-row kr sits in slot c ^ (4 * (kr & 3)): the 4
-// consecutive k-rows x 32 bytes read by a 16-lane ds_read_b64_tr_b16 group
-// fall on distinct banks
-__device__ __forceinline__ uint32_t b_byte(int kr, int c) { return (uint32_t)(kr * 512 + ((c ^ ((kr & 3) << 2)) << 4)); }
-
-template <bool SWIGLU, int BK, int OCC>
-__global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+template <bool SWIGLU, int BK, int OCC, int NJ, int WM>
+__global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                            int64_t max_rows, int E, int K, int N, int ldw,
                                                            const bf16_t* __restrict__ W, bf16_t* __restrict__ Out,
-                                                           int n_tiles) {
-  typedef Geo<BK> GE;
+                                                           int n_tiles, const int32_t* __restrict__ row_token,
+                                                           int64_t a_rows) {
+  typedef Geo<BK, NJ, WM> GE;
+  constexpr int BM = GE::BM, WAVES = GE::WAVES;
+  constexpr int BNB = GE::BNB;
+  constexpr int WCOL = 32 * NJ;       // weight columns per wave
   __shared__ __attribute__((aligned(1024))) char sA0[GE::A_BYTES];
   __shared__ __attribute__((aligned(1024))) char sA1[GE::A_BYTES];
   __shared__ __attribute__((aligned(1024))) char sA2[GE::A_BYTES];
@@ -150,7 +163,7 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
   __shared__ int s_mt[kMaxExperts];
   __shared__ int64_t s_lo[kMaxExperts];
   __shared__ int s_cnt[kMaxExperts];
-  __shared__ int s_wave[NTHR / kWave];
+  __shared__ int s_wave[WAVES];
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -168,7 +181,7 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
     s_mt[tid] = mt;
   }
   int total_mt = 0;
-  const int start = block_exclusive_scan(mt, s_wave, &total_mt);
+  const int start = block_exclusive_scan<WAVES>(mt, s_wave, &total_mt);
   if (tid < E) s_start[tid] = start;
   __syncthreads();
   const int64_t total_tiles = (int64_t)total_mt * n_tiles;
@@ -176,8 +189,8 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
   const int vb = (blockIdx.x % kXcd) * (G / kXcd) + blockIdx.x / kXcd;
 
   auto col_base = [&](int j) {
-    if (SWIGLU) return (j < 2) ? 64 * wn + 32 * j : BNB / 2 + 64 * wn + 32 * (j - 2);
-    return 128 * wn + 32 * j;
+    if (SWIGLU) return (j < NJ / 2) ? (WCOL / 2) * wn + 32 * j : BNB / 2 + (WCOL / 2) * wn + 32 * (j - NJ / 2);
+    return WCOL * wn + 32 * j;
   };
 
   for (int64_t v = vb; v < total_tiles; v += G) {
@@ -204,8 +217,12 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
 
     // Buffer descriptors bound this tile's activation rows and this expert's
     // weights: a load past num_records returns zeros without touching memory.
+    // Activation rows: either rows row0.. of A (expert-ordered rows), or,
+    // with row_token, the token rows row_token[row0 + r] of A read in place
+    // (the permutation's row move fused into this load).
     const __amdgpu_buffer_rsrc_t a_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(A + row0 * K), (short)0, rows * K * 2, kBufferConfig);
+        row_token ? __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(a_rows * K * 2), kBufferConfig)
+                  : __builtin_amdgcn_make_buffer_rsrc((void*)(A + row0 * K), (short)0, rows * K * 2, kBufferConfig);
     const __amdgpu_buffer_rsrc_t b_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)e * K * ldw), (short)0, K * ldw * 2, kBufferConfig);
 
@@ -216,14 +233,17 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
     uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
 #pragma unroll
     for (int p = 0; p < GE::A_INSTR; ++p) {
-      const int r = (wave + 4 * p) * GE::RPI + lane / GE::CPR;
+      const int r = (wave + WAVES * p) * GE::RPI + lane / GE::CPR;
       const int c = (lane % GE::CPR) ^ GE::swz(r);
-      a_voff[p] = (r < rows) ? (uint32_t)(r * K + c * 8) * 2u : kOutOfRange;
+      int64_t src = r;
+      if (row_token) src = (r < rows) ? row_token[row0 + r] : -1;
+      a_voff[p] = (r < rows && src >= 0 && src < (row_token ? a_rows : rows)) ? (uint32_t)(src * K + c * 8) * 2u
+                                                                               : kOutOfRange;
     }
 #pragma unroll
     for (int p = 0; p < GE::B_INSTR; ++p) {
-      const int kr = (wave + 4 * p) * 2 + lane / 32;
-      const int c = (lane % 32) ^ ((kr & 3) << 2);
+      const int kr = (wave + WAVES * p) * GE::BRPI + lane / GE::BCPR;
+      const int c = (lane % GE::BCPR) ^ ((kr & 3) << 2);
       const int tc = c * 8;
       int gcol;
       bool ok;
@@ -245,14 +265,14 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
       const uint32_t a_lds = lds_address(a_buf) + wave * 1024;
       const uint32_t b_lds = lds_address(b_buf) + wave * 1024;
 #pragma unroll
-      for (int p = 0; p < GE::A_INSTR; ++p) dma16(a_rsrc, a_lds + p * 4096, a_voff[p] + ka);
+      for (int p = 0; p < GE::A_INSTR; ++p) dma16(a_rsrc, a_lds + p * WAVES * 1024, a_voff[p] + ka);
 #pragma unroll
-      for (int p = 0; p < GE::B_INSTR; ++p) dma16(b_rsrc, b_lds + p * 4096, b_voff[p] + kb);
+      for (int p = 0; p < GE::B_INSTR; ++p) dma16(b_rsrc, b_lds + p * WAVES * 1024, b_voff[p] + kb);
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[NJ][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -261,21 +281,21 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
     auto compute = [&](const char* a_buf, const char* b_buf) {
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8 a[2], b[4];
+        bf16x8 a[2], b[NJ];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int r = 64 * wm + 32 * i + lane % 32;
           a[i] = *(const bf16x8*)(a_buf + GE::a_byte(r, ks * 2 + lane / 32));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int kr = ks * 16 + (g / 2) * 8 + L / 4;
           const int col = col_base(j) + (g % 2) * 16 + 4 * (L % 4);
-          const uint32_t off = b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
-          b[j] = lds_read_b_operand((const bf16_t*)(b_buf + off), (const bf16_t*)(b_buf + off + 4 * 512));
+          const uint32_t off = GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
+          b[j] = lds_read_b_operand((const bf16_t*)(b_buf + off), (const bf16_t*)(b_buf + off + 4 * GE::BROW));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int i = 0; i < 2; ++i)
             acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
@@ -315,10 +335,10 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
       bf16_t* orow = Out + (row0 + r) * N;
       if (SWIGLU) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const int c = n0 + 64 * wn + 32 * j + 8 * q4 + lc;
+            const int c = n0 + (WCOL / 2) * wn + 32 * j + 8 * q4 + lc;
             if (c >= N) continue;
             uint32_t packed[2];
 #pragma unroll
@@ -326,7 +346,7 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
               float hv[2];
 #pragma unroll
               for (int u = 0; u < 2; ++u) {
-                const float gt = acc[j][i][4 * q4 + 2 * h2 + u], up = acc[j + 2][i][4 * q4 + 2 * h2 + u];
+                const float gt = acc[j][i][4 * q4 + 2 * h2 + u], up = acc[j + NJ / 2][i][4 * q4 + 2 * h2 + u];
                 hv[u] = gt / (1.f + __expf(-gt)) * up;
               }
               packed[h2] = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
@@ -335,10 +355,10 @@ __global__ __launch_bounds__(NTHR, OCC) void k_grouped_gemm(const bf16_t* __rest
           }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const int c = n0 + 128 * wn + 32 * j + 8 * q4 + lc;
+            const int c = n0 + WCOL * wn + 32 * j + 8 * q4 + lc;
             if (c >= N) continue;
             const uint32_t p0 = (uint32_t)f32_to_bf16(acc[j][i][4 * q4]) |
                                 ((uint32_t)f32_to_bf16(acc[j][i][4 * q4 + 1]) << 16);
@@ -427,24 +447,37 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float* __restrict__ 
   y[r * d + c] = acc;
 }
 
-template <bool SWIGLU, int BK = 32, int OCC = 2>
+template <bool SWIGLU, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2>
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
-                      const bf16_t* w, bf16_t* out, hipStream_t s) {
-  const int nt = (int)ceil_div(N, SWIGLU ? dma::BNB / 2 : dma::BNB);
-  dma::k_grouped_gemm<SWIGLU, BK, OCC><<<persistent_grid(max_rows, E, dma::BM, nt, OCC), NTHR, 0, s>>>(
-      a, offsets, max_rows, E, K, N, ldw, w, out, nt);
+                      const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
+                      int64_t a_rows = 0) {
+  constexpr int BNO = SWIGLU ? 32 * NJ : 64 * NJ;   // output columns per tile
+  const int nt = (int)ceil_div(N, BNO);
+  dma::k_grouped_gemm<SWIGLU, BK, OCC, NJ, WM><<<persistent_grid(max_rows, E, 64 * WM, nt, OCC), 128 * WM, 0, s>>>(
+      a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows);
   return hipGetLastError();
 }
 
+// Tile shape from sizes the host knows: 256-row tiles (8 waves sharing each
+// LDS stage, half the weight traffic per flop) once experts hold 256 rows
+// or more on average, 128-row tiles (two workgroups per CU) below that.
+bool wide_rows(int64_t max_rows, int E, int64_t threshold) { return max_rows >= threshold * E; }
+
 }  // namespace
 
-hipError_t launch_gate_up_bf16(const bf16_t* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
-                               int d, int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s) {
-  return launch_dma<true>(x_perm, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s);
+hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
+                               int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s, const int32_t* row_token,
+                               int64_t x_rows) {
+  if (wide_rows(max_rows, E, 256))
+    return launch_dma<true, 32, 1, 4, 4>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token,
+                                         x_rows);
+  return launch_dma<true>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token, x_rows);
 }
 
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s) {
+  if (wide_rows(max_rows, E, 1024))
+    return launch_dma<false, 32, 1, 4, 4>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
   return launch_dma<false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
 }
 
@@ -465,7 +498,7 @@ hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_
 hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets, int64_t max_rows,
                                    int E, int d, int I, const bf16_t* w_gate_up, const bf16_t* w_down,
                                    bf16_t* h, bf16_t* y_perm, hipStream_t s) {
-  const hipError_t e = launch_gate_up_bf16(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s);
+  const hipError_t e = launch_gate_up_bf16(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s, nullptr, 0);
   if (e != hipSuccess) return e;
   return launch_down_bf16(h, expert_offsets, max_rows, E, d, I, w_down, y_perm, s);
 }
