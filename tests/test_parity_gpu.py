@@ -277,7 +277,7 @@ def run_forward(tre, inp, stream=None):
                 pair_row=to_host(pair_row), row_token=to_host(row_token))
 
 
-def check_forward(tre, inp, tokens=None):
+def check_forward(tre, inp, tokens=None, row_tol=None):
     got = run_forward(tre, inp)
     k = inp.k
     if inp.logits is not None:
@@ -299,6 +299,12 @@ def check_forward(tre, inp, tokens=None):
     err = rel_l2(out[sel], ref)
     say(f"  {inp.name}: out rel_l2={err:.3e} over {len(sel)} tokens")
     assert err <= TOL[inp.dtype]
+    if row_tol is not None:
+        # every token on its own (one wrong tile would hide in the whole-array norm)
+        g = as_f64(out[sel])
+        row_err = np.linalg.norm(g - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+        say(f"  worst token rel_l2={row_err.max():.3e}")
+        assert row_err.max() <= row_tol
     return got
 
 
@@ -357,6 +363,18 @@ def test_forward_shapes(tre, T, d, E, k, I, dtype, logits):
     inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype=dtype, seed=T + E, logits=logits)
     say(f"forward T={T} d={d} E={E} k={k} I={I} {dtype}")
     check_forward(tre, inp)
+
+
+@pytest.mark.parametrize("T,d,E,k,I", [
+    (4096, 64, 4, 2, 2048),    # gate/up: K = 64 (two k-stages a tile), >1000 tiles, several per workgroup
+    (8192, 2048, 4, 2, 64),    # down: K = 64, >1000 tiles, several per workgroup
+])
+def test_forward_many_tiles_per_workgroup(tre, T, d, E, k, I):
+    # each persistent workgroup walks several tiles, so the next tile's loads
+    # (and its gathered row index) are issued while the previous tile finishes
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + I, logits="normal_bias")
+    say(f"forward many tiles T={T} d={d} E={E} k={k} I={I}")
+    check_forward(tre, inp, row_tol=TOL["bf16"])
 
 
 def test_forward_all_tokens_one_expert(tre):

@@ -5,8 +5,10 @@
 // [E, d, 2I] weight applied as x @ W and split in two along the last
 // dimension, gate half first.  The down projection (down_proj, "Expert
 // parallelism", section "Overriding plans") is [E, I, d] in the same
-// orientation.  Rows of expert e are [offsets[e], offsets[e+1]) of x_perm:
-//   H[r] = silu(x_perm[r] @ Wgu[e][:, :I]) * (x_perm[r] @ Wgu[e][:, I:])
+// orientation.  Grouped rows of expert e are [offsets[e], offsets[e+1]);
+// grouped row r holds token row_token[r] (or row r of an already grouped
+// copy x_perm):
+//   H[r] = silu(x[row_token[r]] @ Wgu[e][:, :I]) * (x[row_token[r]] @ Wgu[e][:, I:])
 //   Y[r] = H[r] @ Wd[e]
 //
 // bf16 path (MFMA, gfx950), one kernel template with two instances: gate/up
@@ -18,8 +20,12 @@
 //     column j and up column j in the same lane, so SwiGLU is elementwise in
 //     registers;
 //   * k-stages of 32 stream through a ring of three LDS buffers filled by
-//     buffer loads that write LDS directly; two workgroups per CU, so one
-//     workgroup's waits overlap the other's multiplications;
+//     buffer loads that write LDS directly; the stages of all tiles of a
+//     workgroup form one stream, so the next tile's first stages load while
+//     the current tile finishes; two workgroups per CU, so one workgroup's
+//     waits overlap the other's multiplications;
+//   * the gate/up activation loads gather token rows through row_token (the
+//     index of each tile is itself fetched into LDS by DMA a tile ahead);
 //   * weight rows are n-contiguous and reach the MFMA through the gfx950
 //     transposing LDS read ds_read_b64_tr_b16;
 //   * persistent grid: each workgroup derives the tile list from the device
@@ -110,6 +116,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// wait for this wave's LDS reads (lgkmcnt 0), not for vector memory
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 // Stage geometry for k-depth BK (64 or 32) and NJ MFMA column tiles per
 // wave (BNB = 64 NJ weight columns per workgroup tile).  Activation rows hold
 // BK elements (BK/8 chunks of 16 B); a DMA instruction fills 1 KB = RPI
@@ -143,40 +152,70 @@ struct Geo {
   }
 };
 
-template <bool SWIGLU, int BK, int OCC, int NJ, int WM>
-__global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                           int64_t max_rows, int E, int K, int N, int ldw,
-                                                           const bf16_t* __restrict__ W, bf16_t* __restrict__ Out,
-                                                           int n_tiles, const int32_t* __restrict__ row_token,
-                                                           int64_t a_rows) {
+// Where one tile of the work list sits: its expert, its first grouped row,
+// the rows present (at most BM) and its first output column.
+struct Tile {
+  int e;
+  int rows;
+  int64_t row0;
+  int n0;
+};
+
+// Wait until this wave's loads of the stage that has `after` stages issued
+// behind it are complete (loads retire in issue order; at most MAXN stages
+// are ever in flight behind it).
+template <int PER_STAGE, int MAXN>
+__device__ __forceinline__ void wait_for_stage(int64_t after) {
+  if constexpr (MAXN == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= MAXN) wait_vmcnt<MAXN * PER_STAGE>();
+    else wait_for_stage<PER_STAGE, MAXN - 1>(after);
+  }
+}
+
+// The tiles of one workgroup form a single stream of k-stages: stage g of
+// the stream lives in ring buffer g % NS, and while stage g is multiplied,
+// stages g+1 .. g+NS-1 are in flight, whichever tiles they belong to -- so
+// the next tile's first stages load during the current tile's last ones
+// and its epilogue.  With row_token, the grouped-row -> token map of the
+// next tile is fetched into LDS by DMA one tile ahead, so that entering a
+// tile never waits on a plain global load (which would drain the ring).
+template <bool SWIGLU, int BK, int OCC, int NJ, int WM, int NS, bool PP>
+__global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K, int N, int ldw,
+    const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles, const int32_t* __restrict__ row_token,
+    int64_t a_rows) {
   typedef Geo<BK, NJ, WM> GE;
   constexpr int BM = GE::BM, WAVES = GE::WAVES;
   constexpr int BNB = GE::BNB;
-  constexpr int WCOL = 32 * NJ;       // weight columns per wave
-  __shared__ __attribute__((aligned(1024))) char sA0[GE::A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sA1[GE::A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sA2[GE::A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB0[GE::B_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB1[GE::B_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB2[GE::B_BYTES];
+  constexpr int BNO = SWIGLU ? BNB / 2 : BNB;  // output columns per tile
+  constexpr int WCOL = 32 * NJ;                 // weight columns per wave
+  static_assert(NS >= 3 && NS <= 5, "a ring of 3 to 5 stages");
+  static_assert(BM <= 256, "one index DMA covers 256 rows");
+  static_assert(!PP || WAVES == 8, "ping-pong pairs two groups of four waves, one wave of each per SIMD");
+  __shared__ __attribute__((aligned(1024))) char sA[NS * GE::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB[NS * GE::B_BYTES];
+  __shared__ __attribute__((aligned(1024))) int32_t s_rt[2][256];
   __shared__ int s_start[kMaxExperts];
   __shared__ int s_mt[kMaxExperts];
-  __shared__ int64_t s_lo[kMaxExperts];
+  __shared__ int s_lo[kMaxExperts];
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_wave[WAVES];
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 2, wn = wave % 2;
-  const int g = lane / 16, L = lane % 16;
+  const int g16 = lane / 16, L = lane % 16;
 
   // ---- tile list from the device offsets ----
   int mt = 0;
   if (tid < E) {
-    const int64_t lo = clampi<int64_t>(offsets[tid], 0, max_rows);
-    const int64_t hi = clampi<int64_t>(offsets[tid + 1], lo, max_rows);
+    // offsets are int32, so the clamped values fit an int
+    const int lo = (int)clampi<int64_t>(offsets[tid], 0, max_rows);
+    const int hi = (int)clampi<int64_t>(offsets[tid + 1], lo, max_rows);
     s_lo[tid] = lo;
-    s_cnt[tid] = (int)(hi - lo);
+    s_cnt[tid] = hi - lo;
     mt = (int)ceil_div(hi - lo, BM);
     s_mt[tid] = mt;
   }
@@ -187,58 +226,77 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(const bf16_t* __
   const int64_t total_tiles = (int64_t)total_mt * n_tiles;
   const int G = gridDim.x;
   const int vb = (blockIdx.x % kXcd) * (G / kXcd) + blockIdx.x / kXcd;
+  if (vb >= total_tiles) return;  // the whole workgroup: no barrier follows
+  const int64_t my_tiles = (total_tiles - vb + G - 1) / G;
+  const int nk = K / BK;
+  const int64_t total_stages = my_tiles * nk;
+
+  // tile v of the list; `cursor` is the expert of an earlier tile of this
+  // workgroup (tiles are visited in increasing order).  Everything is
+  // wave-uniform and kept in scalar registers.
+  auto decode = [&](int64_t v, int& cursor) {
+    while (cursor + 1 < E && (int64_t)__builtin_amdgcn_readfirstlane(s_start[cursor + 1]) * n_tiles <= v) ++cursor;
+    const int e = __builtin_amdgcn_readfirstlane(cursor);
+    const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
+    const int e_mt = __builtin_amdgcn_readfirstlane(s_mt[e]);
+    const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
+    const int e_lo = __builtin_amdgcn_readfirstlane(s_lo[e]);
+    const int64_t local = v - (int64_t)e_start * n_tiles;
+    const int64_t nt = local / e_mt;
+    const int mtile = (int)(local - nt * e_mt);
+    Tile t;
+    t.e = e;
+    t.row0 = (int64_t)e_lo + (int64_t)mtile * BM;
+    t.rows = min(BM, e_cnt - mtile * BM);
+    t.n0 = (int)nt * BNO;
+    return t;
+  };
 
   auto col_base = [&](int j) {
     if (SWIGLU) return (j < NJ / 2) ? (WCOL / 2) * wn + 32 * j : BNB / 2 + (WCOL / 2) * wn + 32 * (j - NJ / 2);
     return WCOL * wn + 32 * j;
   };
 
-  for (int64_t v = vb; v < total_tiles; v += G) {
-    int lo_e = 0, hi_e = E - 1;
-    while (lo_e < hi_e) {
-      const int mid = (lo_e + hi_e + 1) / 2;
-      if ((int64_t)s_start[mid] * n_tiles <= v) lo_e = mid; else hi_e = mid - 1;
+  // ---- issue side: the tile whose stages are being loaded ----
+  int64_t i_tile = 0;
+  int i_k = 0, i_cursor = 0;
+  Tile inext = decode(vb, i_cursor);  // the tile the issue side enters next
+  __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferConfig);
+  __amdgpu_buffer_rsrc_t b_rsrc = a_rsrc;
+  uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
+
+  // wave 0 copies the token index of grouped rows t.row0 .. t.row0+rows-1
+  // into s_rt[slot] (rows past the tile read as 0 and are never used)
+  auto index_dma = [&](const Tile& t, int slot) {
+    if (wave == 0) {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(row_token + t.row0), (short)0, t.rows * 4, kBufferConfig);
+      dma16(rs, lds_address(&s_rt[slot][0]), (uint32_t)lane * 16u);
     }
-    // every lane found the same tile; say so, so that its addresses and
-    // buffer descriptors live in scalar registers
-    const int e = __builtin_amdgcn_readfirstlane(lo_e);
-    const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
-    const int e_mt = __builtin_amdgcn_readfirstlane(s_mt[e]);
-    const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
-    const int64_t e_lo = s_lo[e];
-    const int64_t e_row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(e_lo >> 32)) << 32) |
-                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)e_lo);
-    const int64_t local = v - (int64_t)e_start * n_tiles;
-    const int nt = (int)(local / e_mt);
-    const int mtile = (int)(local % e_mt);
-    const int64_t row0 = e_row0 + (int64_t)mtile * BM;
-    const int rows = min(BM, e_cnt - mtile * BM);
-    const int n0 = nt * (SWIGLU ? BNB / 2 : BNB);
+  };
 
-    // Buffer descriptors bound this tile's activation rows and this expert's
-    // weights: a load past num_records returns zeros without touching memory.
-    // Activation rows: either rows row0.. of A (expert-ordered rows), or,
-    // with row_token, the token rows row_token[row0 + r] of A read in place
-    // (the permutation's row move fused into this load).
-    const __amdgpu_buffer_rsrc_t a_rsrc =
-        row_token ? __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(a_rows * K * 2), kBufferConfig)
-                  : __builtin_amdgcn_make_buffer_rsrc((void*)(A + row0 * K), (short)0, rows * K * 2, kBufferConfig);
-    const __amdgpu_buffer_rsrc_t b_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)e * K * ldw), (short)0, K * ldw * 2, kBufferConfig);
-
-    // byte offsets at k = 0 (out of range where the row or column does not
-    // exist).  Activation instruction p of this wave fills rows
-    // (wave + 4p) * RPI + lane / CPR; weight instruction p fills k-rows
-    // (wave + 4p) * 2 + lane / 32.
-    uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
+  // Buffer descriptors bound the activation rows (this tile's rows, or with
+  // row_token the whole token matrix) and this expert's weights: a load past
+  // num_records returns zeros.  Activation instruction p of this wave fills
+  // rows (wave + WAVES p) RPI + lane / CPR; weight instruction p fills k-rows
+  // (wave + WAVES p) BRPI + lane / BCPR.
+  auto enter = [&]() {
+    const Tile t = inext;
+    const int slot = (int)(i_tile & 1);
+    a_rsrc = row_token ? __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(a_rows * K * 2), kBufferConfig)
+                       : __builtin_amdgcn_make_buffer_rsrc((void*)(A + t.row0 * K), (short)0, t.rows * K * 2,
+                                                           kBufferConfig);
+    b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)t.e * K * ldw), (short)0, K * ldw * 2,
+                                               kBufferConfig);
 #pragma unroll
     for (int p = 0; p < GE::A_INSTR; ++p) {
       const int r = (wave + WAVES * p) * GE::RPI + lane / GE::CPR;
       const int c = (lane % GE::CPR) ^ GE::swz(r);
       int64_t src = r;
-      if (row_token) src = (r < rows) ? row_token[row0 + r] : -1;
-      a_voff[p] = (r < rows && src >= 0 && src < (row_token ? a_rows : rows)) ? (uint32_t)(src * K + c * 8) * 2u
-                                                                               : kOutOfRange;
+      if (row_token) src = (r < t.rows) ? s_rt[slot][r] : -1;
+      a_voff[p] = (r < t.rows && src >= 0 && src < (row_token ? a_rows : (int64_t)t.rows))
+                      ? (uint32_t)(src * K + c * 8) * 2u
+                      : kOutOfRange;
     }
 #pragma unroll
     for (int p = 0; p < GE::B_INSTR; ++p) {
@@ -248,97 +306,88 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(const bf16_t* __
       int gcol;
       bool ok;
       if (SWIGLU) {
-        const int hc = n0 + (tc % (BNB / 2));
+        const int hc = t.n0 + (tc % (BNB / 2));
         ok = hc < N;
         gcol = (tc < BNB / 2) ? hc : N + hc;
       } else {
-        gcol = n0 + tc;
+        gcol = t.n0 + tc;
         ok = gcol < N;
       }
       b_voff[p] = ok ? (uint32_t)(kr * ldw + gcol) * 2u : kOutOfRange;
     }
-    const int nk = K / BK;
+    if (i_tile + 1 < my_tiles) {
+      inext = decode(vb + (i_tile + 1) * G, i_cursor);
+      if (row_token) index_dma(inext, slot ^ 1);
+    }
+  };
 
-    auto issue = [&](int s, char* a_buf, char* b_buf) {
-      const uint32_t ka = (uint32_t)s * BK * 2u;
-      const uint32_t kb = (uint32_t)s * BK * ldw * 2u;
-      const uint32_t a_lds = lds_address(a_buf) + wave * 1024;
-      const uint32_t b_lds = lds_address(b_buf) + wave * 1024;
+  auto issue_next = [&](int buf) {
+    if (i_k == 0) enter();
+    const uint32_t ka = (uint32_t)i_k * BK * 2u;
+    const uint32_t kb = (uint32_t)i_k * BK * ldw * 2u;
+    const uint32_t a_lds = lds_address(sA + buf * GE::A_BYTES) + wave * 1024;
+    const uint32_t b_lds = lds_address(sB + buf * GE::B_BYTES) + wave * 1024;
 #pragma unroll
-      for (int p = 0; p < GE::A_INSTR; ++p) dma16(a_rsrc, a_lds + p * WAVES * 1024, a_voff[p] + ka);
+    for (int p = 0; p < GE::A_INSTR; ++p) dma16(a_rsrc, a_lds + p * WAVES * 1024, a_voff[p] + ka);
 #pragma unroll
-      for (int p = 0; p < GE::B_INSTR; ++p) dma16(b_rsrc, b_lds + p * WAVES * 1024, b_voff[p] + kb);
-    };
+    for (int p = 0; p < GE::B_INSTR; ++p) dma16(b_rsrc, b_lds + p * WAVES * 1024, b_voff[p] + kb);
+    if (++i_k == nk) {
+      i_k = 0;
+      ++i_tile;
+    }
+  };
 
-    f32x16 acc[NJ][2];
+  // ---- compute side ----
+  f32x16 acc[NJ][2];
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.f;
+  };
 
-    auto compute = [&](const char* a_buf, const char* b_buf) {
+  struct Frag {
+    bf16x8 a[2], b[NJ];
+  };
+  auto read_frag = [&](const char* a_buf, const char* b_buf, int ks, Frag& f) {
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8 a[2], b[NJ];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = 64 * wm + 32 * i + lane % 32;
-          a[i] = *(const bf16x8*)(a_buf + GE::a_byte(r, ks * 2 + lane / 32));
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int kr = ks * 16 + (g / 2) * 8 + L / 4;
-          const int col = col_base(j) + (g % 2) * 16 + 4 * (L % 4);
-          const uint32_t off = GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
-          b[j] = lds_read_b_operand((const bf16_t*)(b_buf + off), (const bf16_t*)(b_buf + off + 4 * GE::BROW));
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
-      }
-    };
-
-    // Stage kt lives in buffer kt % 3.  At step kt each wave waits for its
-    // own loads of stage kt, the barrier makes the whole stage visible and
-    // guarantees every wave is done with stage kt - 1, whose buffer then
-    // receives stage kt + 2.
-    auto step = [&](int kt, const char* a_cur, const char* b_cur, char* a_nxt, char* b_nxt) {
-      if (kt + 1 < nk) wait_vmcnt<GE::PER_STAGE>(); else wait_vmcnt<0>();
-      compiler_fence();
-      __builtin_amdgcn_s_barrier();
-      compiler_fence();
-      if (kt + 2 < nk) issue(kt + 2, a_nxt, b_nxt);
-      compute(a_cur, b_cur);
-    };
-    issue(0, sA0, sB0);
-    if (nk > 1) issue(1, sA1, sB1);
-    for (int kt = 0;;) {
-      step(kt, sA0, sB0, sA2, sB2);
-      if (++kt >= nk) break;
-      step(kt, sA1, sB1, sA0, sB0);
-      if (++kt >= nk) break;
-      step(kt, sA2, sB2, sA1, sB1);
-      if (++kt >= nk) break;
+    for (int i = 0; i < 2; ++i) {
+      const int r = 64 * wm + 32 * i + lane % 32;
+      f.a[i] = *(const bf16x8*)(a_buf + GE::a_byte(r, ks * 2 + lane / 32));
     }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kr = ks * 16 + (g16 / 2) * 8 + L / 4;
+      const int col = col_base(j) + (g16 % 2) * 16 + 4 * (L % 4);
+      const uint32_t off = GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
+      f.b[j] = lds_read_b_operand((const bf16_t*)(b_buf + off), (const bf16_t*)(b_buf + off + 4 * GE::BROW));
+    }
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
+  };
 
-    // ---- epilogue (registers only); acc[j][i] holds output row 64*wm + 32*i + lane%32,
-    // columns col_base(j) + 8*q4 + 4*(lane/32) + {0..3} ----
+  // acc[j][i] holds output row 64 wm + 32 i + lane % 32, columns
+  // col_base(j) + 8 q4 + 4 (lane / 32) + {0..3}
+  auto epilogue = [&](const Tile& t) {
     const int lr = lane % 32, lc = 4 * (lane / 32);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 64 * wm + 32 * i + lr;
-      if (r >= rows) continue;
-      bf16_t* orow = Out + (row0 + r) * N;
+      if (r >= t.rows) continue;
+      bf16_t* orow = Out + (t.row0 + r) * N;
       if (SWIGLU) {
 #pragma unroll
         for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const int c = n0 + (WCOL / 2) * wn + 32 * j + 8 * q4 + lc;
+            const int c = t.n0 + (WCOL / 2) * wn + 32 * j + 8 * q4 + lc;
             if (c >= N) continue;
             uint32_t packed[2];
 #pragma unroll
@@ -358,7 +407,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(const bf16_t* __
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const int c = n0 + WCOL * wn + 32 * j + 8 * q4 + lc;
+            const int c = t.n0 + WCOL * wn + 32 * j + 8 * q4 + lc;
             if (c >= N) continue;
             const uint32_t p0 = (uint32_t)f32_to_bf16(acc[j][i][4 * q4]) |
                                 ((uint32_t)f32_to_bf16(acc[j][i][4 * q4 + 1]) << 16);
@@ -368,11 +417,89 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(const bf16_t* __
           }
       }
     }
-    // the next tile's first loads overwrite buffers 0 and 1: every wave must be
-    // done reading them
+  };
+
+  // ---- the stage stream ----
+  // Every tile has at least NS - 1 stages (the host guarantees it), so the
+  // token index of the next tile, fetched when a tile is entered, has landed
+  // and is visible by the time the next tile is entered.
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (row_token) {
+    // the first tile's index, before anything else is in flight
+    index_dma(inext, 0);
+    wait_vmcnt<0>();
+    barrier();
+  }
+  for (int s = 0; s < NS - 1 && s < total_stages; ++s) issue_next(s);
+
+  int c_k = 0, c_cursor = 0, buf = 0;
+  int64_t c_tile = 0;
+  Tile cur = decode(vb, c_cursor);
+  zero_acc();
+  Frag f0, f1;
+  auto finish_stage = [&]() {
+    buf = (buf + 1 == NS) ? 0 : buf + 1;
+    if (++c_k == nk) {
+      epilogue(cur);
+      zero_acc();
+      c_k = 0;
+      if (++c_tile < my_tiles) cur = decode(vb + c_tile * G, c_cursor);
+    }
+  };
+  if constexpr (!PP) {
+    for (int64_t g = 0; g < total_stages; ++g) {
+      // this wave's loads of stage g are done; after the barrier every
+      // wave's are, and every wave is done reading stage g - 1, whose buffer
+      // ((g - 1) mod NS) then receives stage g + NS - 1
+      wait_for_stage<GE::PER_STAGE, NS - 2>(total_stages - 1 - g);
+      barrier();
+      if (g + NS - 1 < total_stages) issue_next(buf == 0 ? NS - 1 : buf - 1);
+      // all of the stage's fragments first, then its multiplications: the
+      // reads of the second k-step are in flight during the first k-step's
+      // MFMAs
+      read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 0, f0);
+      read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 1, f1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f0);
+      mma(f1);
+      finish_stage();
+    }
+  } else {
+    // Ping-pong: waves 0-3 and waves 4-7 (one of each per SIMD) run the same
+    // body -- read the stage's fragments (and issue the loads of stage
+    // g + NS - 1), barrier, multiply, barrier -- with waves 4-7 one barrier
+    // behind, so that on every SIMD one wave multiplies while the other
+    // reads.  Stage g is read by waves 0-3 between barriers 2g and 2g+1 and
+    // by waves 4-7 between 2g+1 and 2g+2; its buffer is refilled (with stage
+    // g + NS) in the read phase of stage g + 1, which starts after barrier
+    // 2g + 2.  Each wave waits for its own loads of stage g + 1 before the
+    // barrier that ends its read phase of stage g, so every wave's share of
+    // stage g + 1 has landed before barrier 2g + 2.
+    const int grp = wave / 4;
+    wait_for_stage<GE::PER_STAGE, NS - 2>(total_stages - 1);
+    barrier();
+    if (grp == 1) barrier();
+    for (int64_t g = 0; g < total_stages; ++g) {
+      if (g + NS - 1 < total_stages) issue_next(buf == 0 ? NS - 1 : buf - 1);
+      read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 0, f0);
+      read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 1, f1);
+      wait_for_stage<GE::PER_STAGE, NS - 2>(total_stages - 2 - g);
+      wait_lgkm0();
+      barrier();
+      __builtin_amdgcn_s_setprio(1);
+      mma(f0);
+      mma(f1);
+      __builtin_amdgcn_s_setprio(0);
+      finish_stage();
+      barrier();
+    }
+    if (grp == 0) barrier();
   }
 }
 
@@ -447,37 +574,39 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float* __restrict__ 
   y[r * d + c] = acc;
 }
 
-template <bool SWIGLU, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2>
+template <bool SWIGLU, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2, int NS = 3, bool PP = false>
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
                       int64_t a_rows = 0) {
   constexpr int BNO = SWIGLU ? 32 * NJ : 64 * NJ;   // output columns per tile
+  if (K / BK < NS - 1) return hipErrorInvalidValue;  // each tile spans at least NS - 1 stages
   const int nt = (int)ceil_div(N, BNO);
-  dma::k_grouped_gemm<SWIGLU, BK, OCC, NJ, WM><<<persistent_grid(max_rows, E, 64 * WM, nt, OCC), 128 * WM, 0, s>>>(
+  dma::k_grouped_gemm<SWIGLU, BK, OCC, NJ, WM, NS, PP><<<persistent_grid(max_rows, E, 64 * WM, nt, OCC), 128 * WM, 0, s>>>(
       a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows);
   return hipGetLastError();
 }
 
-// Tile shape from sizes the host knows: 256-row tiles (8 waves sharing each
-// LDS stage, half the weight traffic per flop) once experts hold 256 rows
-// or more on average, 128-row tiles (two workgroups per CU) below that.
-bool wide_rows(int64_t max_rows, int E, int64_t threshold) { return max_rows >= threshold * E; }
+// 256-row tiles (8 waves in ping-pong, one workgroup per CU: each weight
+// stage feeds twice the rows) once the experts hold 128 rows or more on
+// average and K spans at least three stages; 128-row tiles (two workgroups
+// per CU) below that.
+bool big_tiles(int64_t max_rows, int E, int K) { return max_rows >= 128 * (int64_t)E && K >= 96; }
 
 }  // namespace
 
 hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s, const int32_t* row_token,
                                int64_t x_rows) {
-  if (wide_rows(max_rows, E, 256))
-    return launch_dma<true, 32, 1, 4, 4>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token,
-                                         x_rows);
+  if (big_tiles(max_rows, E, d))
+    return launch_dma<true, 32, 1, 4, 4, 4, true>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s,
+                                                  row_token, x_rows);
   return launch_dma<true>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token, x_rows);
 }
 
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s) {
-  if (wide_rows(max_rows, E, 1024))
-    return launch_dma<false, 32, 1, 4, 4>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
+  if (big_tiles(max_rows, E, I))
+    return launch_dma<false, 32, 1, 4, 4, 4, true>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
   return launch_dma<false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
 }
 
