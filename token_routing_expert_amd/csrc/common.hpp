@@ -40,7 +40,9 @@ __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return ce
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
                              float* topk_w, hipStream_t s);
 
-// Stable grouping of pairs by expert.  Chunk size of the histogram/scatter.
+// Stable grouping of pairs by expert: per-chunk expert counts (chunks of
+// kPermuteChunk pairs), then the scatter, which also scans the counts when
+// there are few enough of them (else a one-workgroup scan runs between).
 constexpr int kPermuteChunk = 1024;
 size_t permute_index_workspace(int64_t P, int E);
 hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E,

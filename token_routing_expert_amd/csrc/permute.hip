@@ -8,15 +8,20 @@
 //   row_token[r] = token of row r, pair_row[p] = row of pair p (-1: dropped),
 //   x_perm[r] = x[row_token[r]].
 //
-// Three index kernels, all deterministic (no order-dependent atomics):
+// Index kernels, all deterministic (integer counts only; no result depends on
+// the order of atomics):
 //   hist     one workgroup per chunk of kPermuteChunk pairs counts its pairs
-//            per expert in LDS (counts do not depend on atomic order);
-//   scan     one workgroup turns the per-chunk counts into expert offsets and
-//            each chunk's starting row per expert;
-//   scatter  each chunk walks its pairs in order, 256 at a time: a pair's row
-//            is its chunk's running row for the expert, plus the matching
-//            pairs in earlier waves of the step, plus its rank among equal
-//            experts in its own wave (eight ballots over the expert id bits).
+//            per expert in LDS;
+//   scatter  every workgroup first sums the counts of the chunks before its
+//            own and of all chunks (expert offsets and its chunk's starting
+//            row per expert, with no scan kernel in between), then walks its
+//            pairs in order, 256 at a time: a pair's row is its chunk's
+//            running row for the expert, plus the matching pairs in earlier
+//            waves of the step, plus its rank among equal experts in its own
+//            wave (eight ballots over the expert id bits);
+//   scan     only when there are many chunks (the sums above would grow as
+//            chunks^2): one workgroup writes the offsets and every chunk's
+//            starting rows, which the scatter then reads.
 // The row move is a separate, bandwidth-bound kernel: one wave per
 // destination row, 16-byte vectors, rows written in order.
 #include "common.hpp"
@@ -87,16 +92,57 @@ __global__ __launch_bounds__(kThreads) void k_perm_scan(const int32_t* __restric
   if (e == 0) offsets[E] = all;
 }
 
+// chunk_base != nullptr: the chunk starting rows come from k_perm_scan.
+// Otherwise they (and the offsets, written by workgroup 0) are summed here
+// from all n_chunks * E counts.
 __global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __restrict__ pair_expert, int64_t P,
-                                                           int k, int E,
+                                                           int k, int E, int n_chunks,
+                                                           const int32_t* __restrict__ chunk_count,
                                                            const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ pair_row,
                                                            int32_t* __restrict__ row_token) {
   __shared__ int running[kMaxExperts];
+  __shared__ int s_before[kMaxExperts];
+  __shared__ int s_total[kMaxExperts];
   __shared__ int wave_count[kThreads / kWave][kMaxExperts];
+  __shared__ int s_wave[kThreads / kWave];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  if (tid < E) running[tid] = chunk_base[(int64_t)blockIdx.x * E + tid];
-  const int64_t base = (int64_t)blockIdx.x * kPermuteChunk;
+  const int chunk = blockIdx.x;
+  const int64_t base = (int64_t)chunk * kPermuteChunk;
+  const int64_t end = min(P, base + kPermuteChunk);
+  // the first step's expert id, loaded before the counts are summed
+  int e_next = (base + tid < end) ? pair_expert[base + tid] : -1;
+  if (chunk_base) {
+    if (tid < E) running[tid] = chunk_base[(int64_t)chunk * E + tid];
+  } else {
+    if (tid < E) s_before[tid] = s_total[tid] = 0;
+    __syncthreads();
+    // all threads read the counts together, four loads in flight each
+    const int n = n_chunks * E;
+    for (int i0 = tid; i0 < n; i0 += 4 * kThreads) {
+      int c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c[u] = (i0 + u * kThreads < n) ? chunk_count[i0 + u * kThreads] : 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kThreads;
+        if (c[u] != 0) {
+          atomicAdd(&s_total[i % E], c[u]);
+          if (i / E < chunk) atomicAdd(&s_before[i % E], c[u]);
+        }
+      }
+    }
+    __syncthreads();
+    const int total = tid < E ? s_total[tid] : 0;
+    int all = 0;
+    const int start = block_exclusive_scan(total, s_wave, &all);
+    if (tid < E) running[tid] = start + s_before[tid];
+    if (chunk == 0) {
+      if (tid < E) offsets[tid] = start;
+      if (tid == 0) offsets[E] = all;
+    }
+  }
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   for (int step = 0; step < kPermuteChunk; step += kThreads) {
     if (tid < E) {
@@ -105,7 +151,8 @@ __global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __rest
     }
     __syncthreads();
     const int64_t p = base + step + tid;
-    const int e = (p < P) ? pair_expert[p] : -1;
+    const int e = e_next;
+    if (step + kThreads < kPermuteChunk) e_next = (p + kThreads < end) ? pair_expert[p + kThreads] : -1;
     const bool valid = e >= 0 && e < E;
     // lanes of this wave holding the same expert: eight ballots over the id bits
     uint64_t peers = __ballot(valid);
@@ -123,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __rest
       for (int w = 0; w < wave; ++w) r += wave_count[w][e];
       pair_row[p] = r;
       if (r >= 0 && r < P) row_token[r] = (int32_t)(p / k);
-    } else if (p < P) {
+    } else if (p < end) {
       pair_row[p] = -1;
     }
     __syncthreads();
@@ -164,6 +211,9 @@ __global__ __launch_bounds__(kThreads) void k_move_rows(const u32x4* __restrict_
 
 }  // namespace
 
+// Chunk counts up to this many are summed by every scatter workgroup.
+constexpr int64_t kFusedScanMax = 16384;
+
 size_t permute_index_workspace(int64_t P, int E) {
   const int64_t n_chunks = ceil_div(P, kPermuteChunk);
   return (size_t)round_up(2 * n_chunks * E * (int64_t)sizeof(int32_t), 256);
@@ -173,10 +223,14 @@ hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, in
                                 int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s) {
   const int n_chunks = (int)ceil_div(P, kPermuteChunk);
   int32_t* chunk_count = (int32_t*)ws;
-  int32_t* chunk_base = chunk_count + (int64_t)n_chunks * E;
+  int32_t* chunk_base = nullptr;
   k_perm_hist<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, E, chunk_count);
-  k_perm_scan<<<1, kThreads, 0, s>>>(chunk_count, n_chunks, E, chunk_base, expert_offsets);
-  k_perm_scatter<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, k, E, chunk_base, pair_row, row_token);
+  if ((int64_t)n_chunks * E > kFusedScanMax) {
+    chunk_base = chunk_count + (int64_t)n_chunks * E;
+    k_perm_scan<<<1, kThreads, 0, s>>>(chunk_count, n_chunks, E, chunk_base, expert_offsets);
+  }
+  k_perm_scatter<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, k, E, n_chunks, chunk_count, chunk_base,
+                                               expert_offsets, pair_row, row_token);
   return hipGetLastError();
 }
 
