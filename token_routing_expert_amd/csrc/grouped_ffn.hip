@@ -462,12 +462,15 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
       if (g + NS - 1 < total_stages) issue_next(buf == 0 ? NS - 1 : buf - 1);
       // all of the stage's fragments first, then its multiplications: the
       // reads of the second k-step are in flight during the first k-step's
-      // MFMAs
-      read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 0, f0);
-      read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 1, f1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f0);
-      mma(f1);
+      // MFMAs.  A wave whose 64 rows are all past the tile's rows has nothing
+      // to multiply.
+      if (64 * wm < cur.rows) {
+        read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 0, f0);
+        read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 1, f1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f0);
+        mma(f1);
+      }
       finish_stage();
     }
   } else {
@@ -487,15 +490,23 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     if (grp == 1) barrier();
     for (int64_t g = 0; g < total_stages; ++g) {
       if (g + NS - 1 < total_stages) issue_next(buf == 0 ? NS - 1 : buf - 1);
-      read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 0, f0);
-      read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 1, f1);
+      // a wave whose 64 rows are all past the tile's rows has nothing to
+      // multiply: its SIMD then serves the other group alone (tiles of an
+      // expert's last rows run up to twice as fast)
+      const bool active = 64 * wm < cur.rows;
+      if (active) {
+        read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 0, f0);
+        read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 1, f1);
+      }
       wait_for_stage<GE::PER_STAGE, NS - 2>(total_stages - 2 - g);
       wait_lgkm0();
       barrier();
-      __builtin_amdgcn_s_setprio(1);
-      mma(f0);
-      mma(f1);
-      __builtin_amdgcn_s_setprio(0);
+      if (active) {
+        __builtin_amdgcn_s_setprio(1);
+        mma(f0);
+        mma(f1);
+        __builtin_amdgcn_s_setprio(0);
+      }
       finish_stage();
       barrier();
     }
