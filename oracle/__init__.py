@@ -11,6 +11,10 @@ Array conventions: ``x`` and the expert weights are either ``float32`` arrays
 or ``uint16`` arrays of bfloat16 bit patterns; logits are ``float32``.
 
 Steps and the passages they follow (Hugging Face Transformers docs):
+  router     "Expert parallelism", introduction (a router sends each token to
+             its experts) and "Token dispatch" (the router module, mlp.gate /
+             mlp.router): logits = x @ W_r^T with the linear layer's weight
+             W_r [E, d], no bias.
   route      "Expert parallelism", "Adding an implementation" (top_k_index,
              top_k_weights); softmax top-k, ties to the lower expert index.
   dispatch   "Expert parallelism", "Token dispatch": pairs grouped by expert,
@@ -86,6 +90,26 @@ def _dtype_code(a: np.ndarray) -> int:
 def default_threads() -> int:
     n = os.cpu_count() or 1
     return max(1, min(n, 16))
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    """float32 or bfloat16 bits -> float64 (exact)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """Router projection: ``logits[t, e] = sum_c x[t, c] * w_router[e, c]`` in
+    float64 from the exact input values (``x`` [T, d], ``w_router`` [E, d], both
+    float32 or both bfloat16 bits).  The router is the model's gate linear layer
+    ("Expert parallelism", introduction; module mlp.gate / mlp.router in "Token
+    dispatch"); its output feeds the top-k selection as ``route`` takes it."""
+    if x.dtype != w_router.dtype:
+        raise TypeError("x and w_router must share one element type")
+    if x.shape[1] != w_router.shape[1]:
+        raise ValueError(f"shape mismatch: x {x.shape}, w_router {w_router.shape}")
+    return _f64(x) @ _f64(w_router).T
 
 
 def route(logits: np.ndarray, k: int):
