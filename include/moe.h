@@ -71,6 +71,23 @@ const char* moe_status_string(moe_status s);
 moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                           int32_t* topk_idx, float* topk_w, void* stream);
 
+/* Router projection fused with the routing above.  "Expert parallelism",
+ * introduction: a router sends each token to its experts; the router module
+ * is the model's gate linear layer (mlp.gate or mlp.router, "Token
+ * dispatch"), read here as bias-free:
+ *   logits[t, e] = sum_c x[t, c] * w_router[e, c]      (float32 accumulation)
+ * then topk_idx / topk_w exactly as moe_route_topk computes them from those
+ * logits.
+ *   x         [T, d] dt        (d a multiple of 64)
+ *   w_router  [E, d] dt        (the linear layer's weight)
+ *   logits    [T, E] float32   (output; NULL: not written)
+ *   topk_idx  [T, k] int32, topk_w [T, k] float32 (outputs)
+ * Errors: MOE_ERR_ARG for k > E, bad dtype or NULL outputs; MOE_ERR_UNSUPPORTED
+ * for E > 256 or d not a multiple of 64; T == 0 returns MOE_OK.            */
+moe_status moe_route_project(const void* x, const void* w_router, moe_dtype dt, int32_t T, int32_t d,
+                             int32_t E, int32_t k, float* logits, int32_t* topk_idx, float* topk_w,
+                             void* stream);
+
 /* ---- permute --------------------------------------------------------------
  * "Expert parallelism", "Token dispatch": every (token, expert) pair goes to
  * the expert's owner, which runs the expert on the rows it receives.  Here:

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {
         "moe_status_string", "moe_route_topk", "moe_permute_workspace_size", "moe_permute",
         "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
-        "moe_forward_workspace_size", "moe_forward", "moe_gate_up_swiglu", "moe_down_proj"}
+        "moe_forward_workspace_size", "moe_forward", "moe_gate_up_swiglu", "moe_down_proj", "moe_route_project"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -112,6 +112,17 @@ def test_ffn_halves_validation(lib):
     assert g(FAKE, FAKE, 100, 8, 128, 128, FAKE, 1, FAKE, -1, FAKE, None) == 1     # x_rows < 0
     assert g(FAKE, FAKE, 100, 8, 1024, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None) == 2  # x too large for gathering
     assert g(None, None, 0, 8, 128, 128, None, 1, None, 0, None, None) == 0        # no rows
+
+
+def test_route_project_validation(lib):
+    f = lib.moe_route_project
+    assert f(FAKE, FAKE, 1, 10, 128, 8, 9, None, FAKE, FAKE, None) == 1     # k > E
+    assert f(FAKE, FAKE, 1, 10, 128, 300, 2, None, FAKE, FAKE, None) == 2   # E > 256
+    assert f(FAKE, FAKE, 1, 10, 96, 8, 2, None, FAKE, FAKE, None) == 2      # d % 64
+    assert f(FAKE, FAKE, 7, 10, 128, 8, 2, None, FAKE, FAKE, None) == 1     # bad dtype
+    assert f(FAKE, None, 1, 10, 128, 8, 2, None, FAKE, FAKE, None) == 1     # NULL router weight
+    assert f(FAKE, FAKE, 1, 10, 128, 8, 2, None, None, FAKE, None) == 1     # NULL topk_idx
+    assert f(None, None, 1, 0, 128, 8, 2, None, None, None, None) == 0      # T == 0
 
 
 def test_weight_size_limit(lib):

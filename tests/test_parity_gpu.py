@@ -88,6 +88,73 @@ def test_route_empty(tre):
 
 # ---------------------------------------------------------------- permute
 
+def router_inputs(T, d, E, dtype, seed):
+    # router inputs as the workloads draw them: x N(0, 1), W_r N(0, 0.02)
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    w = (0.02 * rng.normal(size=(E, d))).astype(np.float32)
+    if dtype == "bf16":
+        return workloads.bf16_bits(x), workloads.bf16_bits(w)
+    return x, w
+
+
+def check_route_project(tre, x, w_router, k):
+    T, d = x.shape
+    idx, w, lg = tre.moe_route_project(to_device(x), to_device(w_router), k, want_logits=True)
+    sync()
+    lg32 = to_host(lg)
+    ref = oracle.router_logits(x, w_router)
+    # float32 accumulation of d exact (bf16) or once-rounded (f32) products,
+    # in any order: |error| <= 2 d 2^-24 sum_c |x_c w_c|
+    bound = 2 * d * 2.0 ** -24 * (np.abs(as_f64(x)) @ np.abs(as_f64(w_router)).T)
+    err = np.abs(lg32.astype(np.float64) - ref)
+    say(f"route_project T={T} d={d} E={w_router.shape[0]} k={k}: worst |err|/bound {np.max(err / (bound + 1e-300)):.3f}")
+    assert np.all(err <= bound)
+    # routing from the GPU's own logits is exactly the oracle's routing of them
+    ref_idx, ref_w = oracle.route(lg32, k)
+    assert np.array_equal(to_host(idx), ref_idx)
+    assert np.max(np.abs(to_host(w) - ref_w), initial=0) <= W_TOL
+    return lg32
+
+
+@pytest.mark.parametrize("T,d,E,k,dtype", [
+    (4096, 1024, 16, 2, "bf16"),     # the bench layer's router
+    (64, 128, 8, 2, "f32"),          # the float32 layer's router
+    (17, 64, 5, 3, "bf16"),          # ragged token block, E not a multiple of 16
+    (300, 2880, 128, 4, "bf16"),     # wide E, long rows
+    (33, 256, 256, 8, "bf16"),       # the widest E
+    (1, 64, 100, 100, "bf16"),       # one token, k = E
+    (50, 192, 37, 5, "f32"),
+])
+def test_route_project(tre, T, d, E, k, dtype):
+    x, w = router_inputs(T, d, E, dtype, seed=T + d + E)
+    check_route_project(tre, x, w, k)
+
+
+def test_route_project_then_layer(tre):
+    # projection -> routing -> the layer on those pairs equals the oracle layer
+    # fed with the GPU's logits
+    T, d, E, k, I = 600, 256, 8, 2, 192
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=31, logits="normal")
+    _, w_router = router_inputs(T, d, E, "bf16", seed=32)
+    torch = _torch()
+    idx, wt, lg = tre.moe_route_project(to_device(inp.x), to_device(w_router), k, want_logits=True)
+    out, _, _ = tre.moe_forward(to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down), k,
+                                topk_idx=idx, topk_w=wt)
+    sync()
+    ref = oracle.forward(inp.x, inp.w_gate_up, inp.w_down, k, logits=to_host(lg))
+    assert np.array_equal(to_host(idx), ref["idx"])
+    assert rel_l2(to_host(out), ref["out"]) <= TOL["bf16"]
+
+
+def test_route_project_empty(tre):
+    torch = _torch()
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    idx, wt = tre.moe_route_project(x, w, 2)
+    assert idx.shape == (0, 2) and wt.shape == (0, 2)
+
+
 def check_permute(tre, x, pair_expert, k, E):
     torch = _torch()
     T, d = x.shape

@@ -60,6 +60,7 @@ def load(build_if_missing: bool = True):
     sig = {
         "moe_status_string": ([st], ctypes.c_char_p),
         "moe_route_topk": ([p, i32, i32, i32, p, p, p], st),
+        "moe_route_project": ([p, p, st, i32, i32, i32, i32, p, p, p, p], st),
         "moe_permute_workspace_size": ([i32, i32, i32], sz),
         "moe_permute": ([p, st, i32, i32, i32, p, i32, p, p, p, p, p, sz, p], st),
         "moe_grouped_ffn_workspace_size": ([i32, i32, i32, i32, st], sz),
@@ -149,6 +150,29 @@ def moe_route_topk(logits, k: int, topk_idx=None, topk_w=None, stream=None):
     _check("moe_route_topk", lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w),
                                                 _stream(stream)))
     return topk_idx, topk_w
+
+
+def moe_route_project(x, w_router, k: int, want_logits: bool = False, logits=None, topk_idx=None, topk_w=None,
+                      stream=None):
+    """logits = x @ w_router^T (x [T, d], w_router [E, d], float32 accumulation), then
+    top-k routing -> (topk_idx [T, k] int32, topk_w [T, k] float32), plus the logits
+    [T, E] float32 when ``want_logits`` (or when ``logits`` is given)."""
+    torch = _torch()
+    lib = load()
+    T, d = x.shape
+    E, d2 = w_router.shape
+    _expect(w_router, x.dtype, (E, d), "w_router")
+    topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
+    topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
+    _expect(topk_idx, torch.int32, (T, k), "topk_idx")
+    _expect(topk_w, torch.float32, (T, k), "topk_w")
+    if logits is None and want_logits:
+        logits = _empty((T, E), torch.float32, x)
+    if logits is not None:
+        _expect(logits, torch.float32, (T, E), "logits")
+    _check("moe_route_project", lib.moe_route_project(_ptr(x), _ptr(w_router), _dt(x), T, d, E, k, _ptr(logits),
+                                                      _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+    return (topk_idx, topk_w, logits) if logits is not None else (topk_idx, topk_w)
 
 
 def moe_permute(x, pair_expert, k: int, E: int, x_perm=None, row_token=None, pair_row=None,

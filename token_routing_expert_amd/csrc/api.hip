@@ -81,6 +81,24 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
   return from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream));
 }
 
+moe_status moe_route_project(const void* x, const void* w_router, moe_dtype dt, int32_t T, int32_t d, int32_t E,
+                             int32_t k, float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  if (!dtype_ok(dt) || T < 0 || k < 1) return MOE_ERR_ARG;
+  TRY(check_experts(E));
+  if (k > E) return MOE_ERR_ARG;
+  TRY(check_width(d));
+  if ((int64_t)T * d >= kMaxElems || (int64_t)E * d >= kMaxElems || (int64_t)T * E >= kMaxElems)
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == MOE_BF16)
+    return from_hip(launch_route_project_bf16((const bf16_t*)x, (const bf16_t*)w_router, T, d, E, k, logits,
+                                              topk_idx, topk_w, s));
+  return from_hip(launch_route_project_f32((const float*)x, (const float*)w_router, T, d, E, k, logits, topk_idx,
+                                           topk_w, s));
+}
+
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || E < 1) return 0;
   return permute_index_workspace((int64_t)T * k, E);

@@ -39,6 +39,12 @@ __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return ce
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
                              float* topk_w, hipStream_t s);
+// router projection logits = x @ w_router^T (w_router [E, d]) fused with the
+// routing above; logits (float32 [T, E]) written only when non-null
+hipError_t launch_route_project_bf16(const bf16_t* x, const bf16_t* w_router, int T, int d, int E, int k,
+                                    float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s);
+hipError_t launch_route_project_f32(const float* x, const float* w_router, int T, int d, int E, int k,
+                                   float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s);
 
 // Stable grouping of pairs by expert: per-chunk expert counts (chunks of
 // kPermuteChunk pairs), then the scatter, which also scans the counts when

@@ -55,19 +55,17 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Route token t from this lane's logits lg[s] = logit of expert s * G + lane
+// (a group of G lanes per token; the group is wholly active or wholly idle).
 template <int G, int S>
-__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T, int E, int k,
-                                                    int32_t* __restrict__ topk_idx,
-                                                    float* __restrict__ topk_w) {
+__device__ __forceinline__ void route_token(const float (&lg)[S], int64_t t, bool active, int E, int k,
+                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   const int lane = threadIdx.x % G;
-  const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / G;
-  const bool active = t < T;  // a group is either wholly active or wholly idle
-
   uint64_t key[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int e = s * G + lane;
-    key[s] = (active && e < E) ? make_key(logits[t * E + e], e) : 0ull;
+    key[s] = (active && e < E) ? make_key(lg[s], e) : 0ull;
   }
 
   uint64_t sel[S];  // pick j is held by lane j % G in slot j / G
@@ -109,6 +107,22 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
 }
 
 template <int G, int S>
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T, int E, int k,
+                                                    int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ topk_w) {
+  const int lane = threadIdx.x % G;
+  const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / G;
+  const bool active = t < T;
+  float lg[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = s * G + lane;
+    lg[s] = (active && e < E) ? logits[t * E + e] : 0.f;
+  }
+  route_token<G, S>(lg, t, active, E, k, topk_idx, topk_w);
+}
+
+template <int G, int S>
 hipError_t launch(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
   const int per_block = 256 / G;
   const int blocks = (int)ceil_div(T, per_block);
@@ -116,7 +130,161 @@ hipError_t launch(const float* logits, int T, int E, int k, int32_t* idx, float*
   return hipGetLastError();
 }
 
+// ---- router projection fused with routing --------------------------------
+// "Expert parallelism" (introduction: a router sends each token to its
+// experts; the router module is the model's gate linear layer, mlp.gate or
+// mlp.router, "Token dispatch"): logits[t, e] = sum_c x[t, c] * Wr[e, c]
+// with the layer's weight Wr [E, d], float32 accumulation.  A workgroup of
+// four waves takes 16 tokens; wave w sums the columns of quarter w of d, the
+// four partial sums are added in wave order through LDS, and each token is
+// then routed exactly as k_route_topk routes it.
+constexpr int kProjTokens = 16;
+constexpr int kProjWaves = 4;
+
+// bf16: v_mfma_f32_16x16x32_bf16 with 16 router rows (experts) as the first
+// operand and the 16 token rows as the second; both fragments are 16
+// contiguous bytes of a row (lane l: row l % 16, columns 8 (l / 16) .. +7 of
+// the 32-column step).  Lane l receives experts 4 (l / 16) .. +3 of token
+// l % 16.  NEB = 16-expert blocks, one accumulator each.
+template <int NEB>
+__device__ __forceinline__ void project_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int64_t t0,
+                                             int T, int d, int E, float (*s_part)[16 * NEB]) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int tl = lane % 16, q = lane / 16;
+  const bool t_ok = t0 + tl < T;
+  const int steps = d / 32, s0 = wave * steps / kProjWaves, s1 = (wave + 1) * steps / kProjWaves;
+  const bf16_t* xr = x + (t_ok ? t0 + tl : 0) * (int64_t)d + q * 8;
+  const bf16_t* wr[NEB];
+  bool e_ok[NEB];
+#pragma unroll
+  for (int b = 0; b < NEB; ++b) {
+    e_ok[b] = 16 * b + tl < E;
+    wr[b] = w + (int64_t)(e_ok[b] ? 16 * b + tl : 0) * d + q * 8;
+  }
+  bf16x8 zero;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) zero[i] = (__bf16)0.f;
+  f32x4 acc[NEB];
+#pragma unroll
+  for (int b = 0; b < NEB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = NEB >= 8 ? 1 : 4;  // steps whose loads are issued together
+  int st = s0;
+  for (; st + U <= s1; st += U) {
+    bf16x8 xb[U], wb[U][NEB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      xb[u] = t_ok ? *(const bf16x8*)(xr + (st + u) * 32) : zero;
+#pragma unroll
+      for (int b = 0; b < NEB; ++b) wb[u][b] = e_ok[b] ? *(const bf16x8*)(wr[b] + (st + u) * 32) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < NEB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[u][b], xb[u], acc[b], 0, 0, 0);
+  }
+  for (; st < s1; ++st) {
+    const bf16x8 xb = t_ok ? *(const bf16x8*)(xr + st * 32) : zero;
+#pragma unroll
+    for (int b = 0; b < NEB; ++b)
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e_ok[b] ? *(const bf16x8*)(wr[b] + st * 32) : zero, xb,
+                                                       acc[b], 0, 0, 0);
+  }
+#pragma unroll
+  for (int b = 0; b < NEB; ++b)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (16 * b + 4 * q + v < E) s_part[wave * kProjTokens + tl][16 * b + 4 * q + v] = acc[b][v];
+}
+
+// float32: per-lane dot products in ascending column order over the wave's
+// quarter of d (lane l: token l % 16, experts l / 16, l / 16 + 4, ...).
+template <int NEB>
+__device__ __forceinline__ void project_f32(const float* __restrict__ x, const float* __restrict__ w, int64_t t0,
+                                            int T, int d, int E, float (*s_part)[16 * NEB]) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int tl = lane % 16, q = lane / 16;
+  if (t0 + tl >= T) return;
+  const int c0 = wave * d / kProjWaves, c1 = (wave + 1) * d / kProjWaves;
+  const float* xr = x + (t0 + tl) * (int64_t)d;
+  for (int e = q; e < E; e += 4) {
+    const float* wrow = w + (int64_t)e * d;
+    float acc = 0.f;
+    for (int c = c0; c < c1; ++c) acc = fmaf(xr[c], wrow[c], acc);
+    s_part[wave * kProjTokens + tl][e] = acc;
+  }
+}
+
+template <typename Elem, int G, int S, int NEB>
+__global__ __launch_bounds__(kProjWaves * kWave) void k_route_project(
+    const Elem* __restrict__ x, const Elem* __restrict__ w, int T, int d, int E, int k, float* __restrict__ logits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  __shared__ float s_part[kProjWaves * kProjTokens][16 * NEB];  // E <= 16 NEB
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * kProjTokens;
+  if constexpr (sizeof(Elem) == 2)
+    project_bf16<NEB>(x, w, t0, T, d, E, s_part);
+  else
+    project_f32<NEB>(x, w, t0, T, d, E, s_part);
+  __syncthreads();
+  // the four quarters of d, added in order, into the first wave's rows
+  for (int i = tid; i < kProjTokens * E; i += kProjWaves * kWave) {
+    const int tl = i / E, e = i % E;
+    if (t0 + tl >= T) continue;
+    float v = s_part[tl][e];
+#pragma unroll
+    for (int wq = 1; wq < kProjWaves; ++wq) v += s_part[wq * kProjTokens + tl][e];
+    s_part[tl][e] = v;
+    if (logits) logits[(t0 + tl) * E + e] = v;
+  }
+  __syncthreads();
+  // G lanes per token, 256 / G tokens at a time
+  constexpr int per_pass = kProjWaves * kWave / G;
+#pragma unroll
+  for (int pass = 0; pass < (kProjTokens + per_pass - 1) / per_pass; ++pass) {
+    const int tl = pass * per_pass + tid / G;
+    const int64_t t = t0 + tl;
+    const bool active = tl < kProjTokens && t < T;
+    float lg[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int e = s * G + tid % G;
+      lg[s] = (active && e < E) ? s_part[tl][e] : 0.f;
+    }
+    route_token<G, S>(lg, t, active, E, k, topk_idx, topk_w);
+  }
+}
+
+template <typename Elem, int G, int S, int NEB>
+hipError_t launch_project(const Elem* x, const Elem* w, int T, int d, int E, int k, float* logits, int32_t* idx,
+                          float* wt, hipStream_t s) {
+  k_route_project<Elem, G, S, NEB><<<(unsigned)ceil_div(T, kProjTokens), kProjWaves * kWave, 0, s>>>(
+      x, w, T, d, E, k, logits, idx, wt);
+  return hipGetLastError();
+}
+
+template <typename Elem>
+hipError_t dispatch_project(const Elem* x, const Elem* w, int T, int d, int E, int k, float* logits, int32_t* idx,
+                            float* wt, hipStream_t s) {
+  if (E <= 8) return launch_project<Elem, 8, 1, 1>(x, w, T, d, E, k, logits, idx, wt, s);
+  if (E <= 16) return launch_project<Elem, 16, 1, 1>(x, w, T, d, E, k, logits, idx, wt, s);
+  if (E <= 32) return launch_project<Elem, 32, 1, 2>(x, w, T, d, E, k, logits, idx, wt, s);
+  if (E <= 64) return launch_project<Elem, 64, 1, 4>(x, w, T, d, E, k, logits, idx, wt, s);
+  if (E <= 128) return launch_project<Elem, 64, 2, 8>(x, w, T, d, E, k, logits, idx, wt, s);
+  return launch_project<Elem, 64, 4, 16>(x, w, T, d, E, k, logits, idx, wt, s);
+}
+
 }  // namespace
+
+hipError_t launch_route_project_bf16(const bf16_t* x, const bf16_t* w_router, int T, int d, int E, int k,
+                                    float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  return dispatch_project<bf16_t>(x, w_router, T, d, E, k, logits, topk_idx, topk_w, s);
+}
+
+hipError_t launch_route_project_f32(const float* x, const float* w_router, int T, int d, int E, int k,
+                                   float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  return dispatch_project<float>(x, w_router, T, d, E, k, logits, topk_idx, topk_w, s);
+}
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
                              float* topk_w, hipStream_t s) {
