@@ -125,6 +125,8 @@ def check_route_project(tre, x, w_router, k):
     (33, 256, 256, 8, "bf16"),       # the widest E
     (1, 64, 100, 100, "bf16"),       # one token, k = E
     (50, 192, 37, 5, "f32"),
+    (2100, 256, 64, 2, "bf16"),      # many workgroups, ragged last one
+    (2048, 512, 256, 8, "bf16"),     # the widest E over a larger batch
 ])
 def test_route_project(tre, T, d, E, k, dtype):
     x, w = router_inputs(T, d, E, dtype, seed=T + d + E)
