@@ -254,6 +254,37 @@ def main() -> int:
                 for i, name in enumerate(STAGES)}
     gpu_ms = float(np.mean([evs[st][0].elapsed_time(evs[st][len(STAGES)]) for st in range(args.steps)]))
 
+    # ---- timed region 3 (reported beside the layer, not part of it): the
+    # router projection fused with routing, x @ W_r^T then top-k, on the
+    # workload's tokens and a seeded router weight [E, d] ----
+    router = None
+    if logits is not None:
+        w_r = to_device(workloads.router_weight(inp), torch)
+        r_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        r_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+
+        def run_router():
+            st = lib.moe_route_project(ptr(x), ptr(w_r), dt, T, d, E, k, None, ptr(r_idx), ptr(r_w), sp)
+            if st != 0:
+                raise RuntimeError(f"moe_route_project failed with status {st}")
+        for _ in range(args.warmup):
+            run_router()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run_router()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        r_ms = ev0.elapsed_time(ev1) / args.steps
+        s_el = 4 if inp.dtype == "f32" else 2
+        r_bytes = T * d * s_el + E * d * s_el + 8 * T * k
+        r_flops = 2 * T * d * E
+        router = {"ms": round(r_ms, 5), "bound": "hbm", "bytes_per_launch": r_bytes,
+                  "gbs": round(r_bytes / (r_ms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(r_bytes / (r_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "tflops": round(r_flops / (r_ms * 1e-3) / 1e12, 2)}
+
     work = algorithmic_work(inp, n_rows, live)
     peak_mm = PEAK_F32_TFLOPS if inp.dtype == "f32" else PEAK_BF16_TFLOPS
     kernels = {}
@@ -307,6 +338,7 @@ def main() -> int:
         "staged_ms_per_step": staged_ms,
         "staged_gpu_ms_per_step": gpu_ms,
         "permute_gbs": kernels["permute"].get("gbs"),
+        "router_projection": router,
     }
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

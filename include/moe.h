@@ -83,7 +83,7 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
  *   logits    [T, E] float32   (output; NULL: not written)
  *   topk_idx  [T, k] int32, topk_w [T, k] float32 (outputs)
  * Errors: MOE_ERR_ARG for k > E, bad dtype or NULL outputs; MOE_ERR_UNSUPPORTED
- * for E > 256 or d not a multiple of 64; T == 0 returns MOE_OK.            */
+ * for E > 256, d not a multiple of 64 or d >= 2^22; T == 0 returns MOE_OK. */
 moe_status moe_route_project(const void* x, const void* w_router, moe_dtype dt, int32_t T, int32_t d,
                              int32_t E, int32_t k, float* logits, int32_t* topk_idx, float* topk_w,
                              void* stream);

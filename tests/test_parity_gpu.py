@@ -127,6 +127,9 @@ def check_route_project(tre, x, w_router, k):
     (50, 192, 37, 5, "f32"),
     (2100, 256, 64, 2, "bf16"),      # many workgroups, ragged last one
     (2048, 512, 256, 8, "bf16"),     # the widest E over a larger batch
+    (4100, 320, 128, 4, "bf16"),     # 32-token workgroups, ragged last one
+    (40, 128, 33, 3, "bf16"),        # staged kernel with most of the last expert block empty
+    (8192, 2880, 128, 4, "bf16"),    # the large layer's router at full size
 ])
 def test_route_project(tre, T, d, E, k, dtype):
     x, w = router_inputs(T, d, E, dtype, seed=T + d + E)

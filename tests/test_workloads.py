@@ -78,3 +78,16 @@ def test_config_table_matches_definition():
     assert (c["decode"]["T"], c["decode"]["d"], c["decode"]["E"], c["decode"]["k"],
             c["decode"]["I"]) == (64, 5120, 16, 1, 8192)
     assert workloads.ORDER[1] == "small_bf16"
+
+
+def test_router_weight_layout():
+    # the gate linear layer's weight [E, d]: its transpose is the W_r [d, E]
+    # that the tiny workload's logits were drawn with
+    inp = make("tiny_f32", weights=False)
+    wr = workloads.router_weight(inp)
+    assert wr.shape == (inp.E, inp.d) and wr.dtype == np.float32 and wr.flags.c_contiguous
+    lg = (inp.x.astype(np.float64) @ wr.astype(np.float64).T).astype(np.float32)
+    assert np.array_equal(lg, inp.logits)
+    big = workloads.router_weight("large_e128")
+    assert big.shape == (128, 2880) and big.dtype == np.uint16
+    assert 0.015 < float(np.std(to_float32(big))) < 0.025

@@ -9,6 +9,7 @@ using namespace tre;
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;  // per-array element limit
+constexpr int32_t kMaxRouterWidth = 1 << 22;       // router projection: d below this
 
 size_t elem_size(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
 bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
@@ -89,6 +90,8 @@ moe_status moe_route_project(const void* x, const void* w_router, moe_dtype dt, 
   TRY(check_width(d));
   if ((int64_t)T * d >= kMaxElems || (int64_t)E * d >= kMaxElems || (int64_t)T * E >= kMaxElems)
     return MOE_ERR_UNSUPPORTED;
+  // byte offsets into 256 router rows stay below 2^31
+  if (d >= kMaxRouterWidth) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_ARG;
   hipStream_t s = (hipStream_t)stream;

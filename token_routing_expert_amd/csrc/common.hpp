@@ -35,6 +35,48 @@ __device__ __forceinline__ T clampi(T v, T lo, T hi) {
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// ---- loads that write LDS directly (the GEMM and the router projection) ----
+
+// Buffer descriptor word 3 for raw (untyped) buffer loads on CDNA.  A load at
+// a byte offset past num_records returns zeros.
+constexpr int kBufferConfig = 0x00020000;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  // vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) not waited on
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS (address space 3) byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One wave-wide 16-byte-per-lane buffer load written straight to LDS at
+// lds_base + 16 * lane.  Issued as inline assembly so that the compiler does
+// not wait on it conservatively before unrelated LDS reads; completion is
+// tracked explicitly with wait_vmcnt, visibility with a workgroup barrier.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier that neither the scheduler nor the compiler's memory
+// model moves work across, and that does not drain outstanding LDS-writing
+// loads the way __syncthreads() does.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,

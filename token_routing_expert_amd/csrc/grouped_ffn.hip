@@ -42,9 +42,7 @@ namespace {
 
 constexpr int NTHR = 256;        // 4 waves per workgroup
 constexpr int kXcd = 8;          // XCDs per MI355X; workgroups are dealt round-robin over them
-// Buffer descriptor word 3 for raw (untyped) buffer loads on CDNA, and byte
-// offsets that are always past num_records (a load there returns zeros).
-constexpr int kBufferConfig = 0x00020000;
+// byte offset that is always past num_records (a buffer load there returns zeros)
 constexpr uint32_t kOutOfRange = 0x80000000u;
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -90,31 +88,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
 // consecutive k-rows x 32 bytes per 16-lane group) touch every bank once.
 namespace dma {
 
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  // vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) not waited on
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// LDS (address space 3) byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// One wave-wide 16-byte-per-lane buffer load written straight to LDS at
-// lds_base + 16 * lane.  Issued as inline assembly so that the compiler does
-// not wait on it conservatively before unrelated LDS reads; completion is
-// tracked explicitly with wait_vmcnt, visibility with the stage barrier.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_base), "v"(voffset), "s"(rsrc)
-               : "memory");
-}
-
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // wait for this wave's LDS reads (lgkmcnt 0), not for vector memory
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
@@ -423,13 +396,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   // Every tile has at least NS - 1 stages (the host guarantees it), so the
   // token index of the next tile, fetched when a tile is entered, has landed
   // and is visible by the time the next tile is entered.
-  auto barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    compiler_fence();
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    __builtin_amdgcn_sched_barrier(0);
-  };
+  auto barrier = [&]() { stage_barrier(); };
   if (row_token) {
     // the first tile's index, before anything else is in flight
     index_dma(inext, 0);

@@ -179,6 +179,18 @@ def make_custom(T: int, d: int, E: int, k: int, I: int, dtype: str = "bf16", see
                   logits=lg, pair_expert=pe, pair_w=pw)
 
 
+def router_weight(name_or_inputs, seed: int | None = None) -> np.ndarray:
+    """The router (gate linear layer) weight of a workload, laid out as that
+    layer stores it: [E, d], N(0, 0.02), in the workload's element type.  It
+    is the transpose of the W_r [d, E] that the "router" logits recipe draws
+    (same stream), so on tiny_f32 x @ W_r reproduces the workload's logits."""
+    inp = name_or_inputs if isinstance(name_or_inputs, Inputs) else make(name_or_inputs, weights=False)
+    cfg_seed = CONFIGS[inp.name]["seed"] if inp.name in CONFIGS else 0
+    wr = _normal(cfg_seed if seed is None else seed, _TAG_ROUTER, 0, (inp.d, inp.E), WEIGHT_STD)
+    wt = np.ascontiguousarray(wr.T)
+    return wt if inp.dtype == "f32" else bf16_bits(wt)
+
+
 def to_float32(a: np.ndarray) -> np.ndarray:
     """Decode an array of either element type to float32 (bf16 bits are exact in float32)."""
     if a.dtype == np.float32:
