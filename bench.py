@@ -254,6 +254,29 @@ def main() -> int:
                 for i, name in enumerate(STAGES)}
     gpu_ms = float(np.mean([evs[st][0].elapsed_time(evs[st][len(STAGES)]) for st in range(args.steps)]))
 
+    # ---- timed region 2b: the same layer captured once as a HIP graph and
+    # replayed K times (what a decode loop would do; the library records no
+    # host work, so the whole layer is one graph) ----
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        st = lib.moe_forward(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(topk_idx),
+                             ptr(topk_w), None, None, None, ptr(out), ptr(fws), fws_bytes, cap.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"moe_forward (captured) failed with status {st}")
+    for _ in range(args.warmup):
+        graph.replay()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graph
+
     # ---- timed region 3 (reported beside the layer, not part of it): the
     # router projection fused with routing, x @ W_r^T then top-k, on the
     # workload's tokens and a seeded router weight [E, d] ----
@@ -337,6 +360,7 @@ def main() -> int:
         "kernels": kernels,
         "staged_ms_per_step": staged_ms,
         "staged_gpu_ms_per_step": gpu_ms,
+        "graph_ms_per_step": graph_ms,
         "permute_gbs": kernels["permute"].get("gbs"),
         "router_projection": router,
     }

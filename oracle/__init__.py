@@ -22,6 +22,12 @@ Steps and the passages they follow (Hugging Face Transformers docs):
   experts    "Tensor parallelism for inference", "Packed strategies": packed
              gate/up weight [E, d, 2I], hidden @ W, gate half first; SwiGLU.
   combine    "Expert parallelism", "Token dispatch": routing-weighted sum.
+  backward   "Expert parallelism", "Adding an implementation" (gradients, the
+             routing weights' included, must reach every rank that holds
+             tokens) and "Combining with FSDP2" (an expert's gradient sums
+             over every batch it served; an expert that received no tokens
+             still takes part, with a zero gradient): the chain rule through
+             the steps above, in float64 (``backward``).
 """
 from __future__ import annotations
 
@@ -226,3 +232,76 @@ def combine(y_perm: np.ndarray, pair_row: np.ndarray, pair_w: np.ndarray, T: int
             if 0 <= r < y.shape[0]:
                 out[t] += pair_w[t * k + j] * y[r]
     return out
+
+
+def _expand(a: np.ndarray) -> np.ndarray:
+    """float64 copy of a float32 array or of bfloat16 bits (both exact)."""
+    return _f64(a)
+
+
+def backward(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray, k: int, dout: np.ndarray,
+             logits=None, pair_expert=None, pair_w=None) -> dict:
+    """Gradients of the layer's output, contracted with ``dout`` [T, d]: the
+    chain rule through combine, down projection, SwiGLU, gate/up projection
+    and (with ``logits``) the renormalised softmax, in float64 with one
+    matmul per expert.  The top-k selection itself is piecewise constant and
+    passes no gradient.
+
+    For pair p = (t, j) with expert e, row x_t, weight w_p:
+      g = x_t Wg_e, u = x_t Wu_e, s = sigmoid(g), h = g s u, y_p = h Wd_e
+      out_t = sum_j w_p y_p
+    so, with dy_p = w_p dout_t:
+      dw_p   = <dout_t, y_p>
+      dh     = dy_p Wd_e^T,            dWd_e  += h^T dy_p
+      dg     = dh u s (1 + g (1 - s)), du = dh g s
+      dx_t  += dg Wg_e^T + du Wu_e^T,  dWg_e += x_t^T dg, dWu_e += x_t^T du
+    and, when the weights come from logits (w_j = softmax of the selected
+    logits), dlogit_{t, e_j} = w_j (dw_j - sum_i w_i dw_i), zero for experts
+    not selected.
+
+    Pairs with expert -1 are skipped.  Returns a dict of float64 arrays
+    ``dx [T, d], dw_gate_up [E, d, 2I], dw_down [E, I, d], dw [T, k]`` and
+    ``dlogits [T, E]`` (when ``logits`` is given), plus ``idx`` and ``w``.
+    """
+    X = _expand(x)
+    Wgu = _expand(w_gate_up)
+    Wd = _expand(w_down)
+    dO = np.asarray(dout, dtype=np.float64)
+    T, d = X.shape
+    E, _, two_i = Wgu.shape
+    I = two_i // 2
+    if logits is not None:
+        idx, w = route(logits, k)
+    else:
+        idx = np.asarray(pair_expert, dtype=np.int32).reshape(T, k)
+        w = np.asarray(pair_w, dtype=np.float64).reshape(T, k)
+    dx = np.zeros((T, d))
+    dwgu = np.zeros((E, d, 2 * I))
+    dwd = np.zeros((E, I, d))
+    dw = np.zeros((T, k))
+    for e in range(E):
+        tt, jj = np.nonzero(idx == e)  # the pairs of expert e (t ascending, then j)
+        if tt.size == 0:
+            continue
+        xe = X[tt]
+        g = xe @ Wgu[e][:, :I]
+        u = xe @ Wgu[e][:, I:]
+        s = 1.0 / (1.0 + np.exp(-g))
+        h = g * s * u
+        y = h @ Wd[e]
+        dw[tt, jj] = np.sum(dO[tt] * y, axis=1)
+        dy = w[tt, jj][:, None] * dO[tt]
+        dh = dy @ Wd[e].T
+        dwd[e] = h.T @ dy
+        dg = dh * u * s * (1.0 + g * (1.0 - s))
+        du = dh * g * s
+        dwgu[e][:, :I] = xe.T @ dg
+        dwgu[e][:, I:] = xe.T @ du
+        np.add.at(dx, tt, dg @ Wgu[e][:, :I].T + du @ Wgu[e][:, I:].T)
+    res = dict(idx=idx, w=w, dx=dx, dw_gate_up=dwgu, dw_down=dwd, dw=dw)
+    if logits is not None:
+        dl = np.zeros((T, E))
+        inner = np.sum(w * dw, axis=1, keepdims=True)
+        np.put_along_axis(dl, idx.astype(np.int64), w * (dw - inner), axis=1)
+        res["dlogits"] = dl
+    return res

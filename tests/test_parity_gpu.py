@@ -496,3 +496,67 @@ def test_forward_empty_batch(tre):
     out, idx, w = tre.moe_forward(x, wgu, wd, 2, logits=torch.zeros((0, 4), dtype=torch.float32, device="cuda"))
     sync()
     assert out.shape == (0, 128)
+
+
+def test_forward_graph_replay_masked_experts(tre):
+    # One rank's share of the masked expert-parallel layout (the "all_reduce"
+    # implementation of "Choosing an implementation"): every pair whose expert
+    # lies outside this rank's block of four experts carries id -1 and is
+    # skipped.  The layer is captured once as a graph and replayed on fresh
+    # tokens and routings copied into the captured buffers, with eager work in
+    # between; every replay equals an eager call bit for bit and the oracle.
+    torch = _torch()
+    T, d, E, k, I = 64, 256, 16, 2, 320
+    lo, hi = 4, 8
+    base = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=41, logits="normal")
+    wgu, wd = to_device(base.w_gate_up), to_device(base.w_down)
+    x_g = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    idx_g = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w_g = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out_g = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    ws_g = torch.empty(tre.moe_forward_workspace_size(T, d, E, k, I, tre.MOE_BF16), dtype=torch.uint8,
+                       device="cuda")
+
+    def rank_inputs(seed):
+        rng = np.random.default_rng(seed)
+        x = workloads.bf16_bits(rng.normal(size=(T, d)).astype(np.float32))
+        idx, w = oracle.route(rng.normal(size=(T, E)).astype(np.float32), k)
+        idx = np.where((idx >= lo) & (idx < hi), idx, -1).astype(np.int32)
+        return x, idx, w.astype(np.float32)
+
+    def load(seed):
+        x, idx, w = rank_inputs(seed)
+        x_g.copy_(to_device(x))
+        idx_g.copy_(to_device(idx))
+        w_g.copy_(to_device(w))
+        return x, idx, w
+
+    def layer():
+        tre.moe_forward(x_g, wgu, wd, k, topk_idx=idx_g, topk_w=w_g, out=out_g, workspace=ws_g)
+
+    load(100)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    sync()
+    for rep in range(3):
+        x, idx, w = load(101 + rep)
+        graph.replay()
+        sync()
+        replayed = to_host(out_g).copy()
+        eager, _, _ = tre.moe_forward(x_g, wgu, wd, k, topk_idx=idx_g, topk_w=w_g)
+        sync()
+        assert np.array_equal(replayed, to_host(eager)), f"replay {rep}"
+        ref = oracle.moe_tokens(x, idx, w.astype(np.float64), base.w_gate_up, base.w_down)
+        err = rel_l2(replayed, ref)
+        say(f"  graph replay {rep}: {int((idx >= 0).sum())} local pairs, out rel_l2={err:.3e}")
+        assert err <= TOL["bf16"]
+        # tokens with no local pair come out exactly zero
+        none = np.all(idx < 0, axis=1)
+        assert np.all(replayed[none] == 0)
