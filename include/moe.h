@@ -176,6 +176,40 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
                        int32_t* pair_row, void* out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ---- the layer's backward pass ----------------------------------------------
+ * "Expert parallelism", "Adding an implementation": gradients, the routing
+ * weights' included, must reach the rank that holds the tokens; "Combining
+ * with FSDP2": an expert's weight gradient sums over every row it served (an
+ * expert without rows gets a zero gradient).  Gradients of <dout, out> with
+ * out = moe_forward(x, ...) on the same arguments, by the chain rule:
+ *   pair p = (t, j) with expert e, weight w_p, x row x_t:
+ *     g = x_t Wg[e], u = x_t Wu[e], s = sigmoid(g), h = g s u, y_p = h Wd[e]
+ *     dtopk_w[p] = <dout_t, y_p>;   dy_p = w_p dout_t
+ *     dW_down[e] = sum_p h^T dy_p;  dh = dy_p Wd[e]^T
+ *     dg = dh u s (1 + g (1 - s));  du = dh g s
+ *     dW_gate_up[e] = sum_p x_t^T [dg | du];  dx_t = sum_j [dg | du] Wgu[e]^T
+ *     with logits: dlogits[t, e_j] = w_j (dtopk_w_j - sum_i w_i dtopk_w_i),
+ *     zero for experts not selected (the selection passes no gradient).
+ * The forward is recomputed inside (routing when logits are given, the
+ * grouping, both projections).  bf16 only: bf16 operands and stored
+ * intermediates (the pre-activations g, u, h, y and the row gradients),
+ * float32 accumulation, gradients rounded to bf16 (dtopk_w, dlogits float32).
+ *   x, dout [T, d] bf16; w_gate_up [E, d, 2I], w_down [E, I, d] bf16
+ *   logits [T, E] float32 or NULL, and topk_idx / topk_w [T, k], as for
+ *     moe_forward (outputs with logits, inputs without; -1 ids are skipped)
+ *   dx [T, d], dw_gate_up [E, d, 2I], dw_down [E, I, d] bf16 (outputs,
+ *     overwritten); dtopk_w [T, k] float32 (output, 0 for skipped pairs);
+ *     dlogits [T, E] float32 (output; NULL to skip; only with logits)
+ *   workspace >= moe_backward_workspace_size(T, d, E, k, I, dt) bytes
+ * Errors: as moe_forward; MOE_ERR_UNSUPPORTED for dt = MOE_F32; MOE_ERR_ARG
+ * for dlogits without logits.  T == 0 zeroes the weight gradients only.    */
+size_t moe_backward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, moe_dtype dt);
+moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                        int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt,
+                        int32_t* topk_idx, float* topk_w, const void* dout, void* dx, void* dw_gate_up,
+                        void* dw_down, float* dtopk_w, float* dlogits, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {
         "moe_status_string", "moe_route_topk", "moe_permute_workspace_size", "moe_permute",
         "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
-        "moe_forward_workspace_size", "moe_forward", "moe_gate_up_swiglu", "moe_down_proj", "moe_route_project"}
+        "moe_forward_workspace_size", "moe_forward", "moe_gate_up_swiglu", "moe_down_proj", "moe_route_project",
+        "moe_backward_workspace_size", "moe_backward"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -123,6 +124,31 @@ def test_route_project_validation(lib):
     assert f(FAKE, None, 1, 10, 128, 8, 2, None, FAKE, FAKE, None) == 1     # NULL router weight
     assert f(FAKE, FAKE, 1, 10, 128, 8, 2, None, None, FAKE, None) == 1     # NULL topk_idx
     assert f(None, None, 1, 0, 128, 8, 2, None, None, None, None) == 0      # T == 0
+    assert f(FAKE, FAKE, 1, 10, 1 << 22, 8, 2, None, FAKE, FAKE, None) == 2  # d >= 2^22
+
+
+def test_backward_validation(lib):
+    f = lib.moe_backward
+
+    def call(x=FAKE, logits=FAKE, T=10, d=128, E=8, k=2, I=64, dt=1, dout=FAKE, dlogits=FAKE, ws=FAKE,
+             ws_bytes=0):
+        return f(x, logits, T, d, E, k, I, FAKE, FAKE, dt, FAKE, FAKE, dout, FAKE, FAKE, FAKE, FAKE, dlogits,
+                 ws, ws_bytes, None)
+    assert call(dt=0) == 2                    # float32: not supported
+    assert call(dt=5) == 1                    # bad dtype
+    assert call(k=9) == 1                     # k > E with logits
+    assert call(E=300) == 2                   # E > 256
+    assert call(d=96) == 2                    # d % 64
+    assert call(I=100) == 2                   # I % 64
+    assert call(logits=None) == 1             # dlogits without logits
+    assert call(dout=None) == 1               # NULL upstream gradient
+    assert call(x=None) == 1
+    assert call(ws_bytes=1024) == 3           # workspace too small
+    need = lib.moe_backward_workspace_size(10, 128, 8, 2, 64, 1)
+    assert call(ws=None, ws_bytes=need) == 3  # no workspace
+    assert lib.moe_backward_workspace_size(10, 128, 8, 2, 64, 0) == 0
+    assert need > lib.moe_forward_workspace_size(10, 128, 8, 2, 64, 1)
+    assert lib.moe_backward_workspace_size(20, 128, 8, 2, 64, 1) > need
 
 
 def test_weight_size_limit(lib):

@@ -560,3 +560,100 @@ def test_forward_graph_replay_masked_experts(tre):
         # tokens with no local pair come out exactly zero
         none = np.all(idx < 0, axis=1)
         assert np.all(replayed[none] == 0)
+
+
+# ---------------------------------------------------------------- backward
+
+def run_backward(tre, inp, dout_bits):
+    x, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
+    if inp.logits is not None:
+        res = tre.moe_backward(x, wgu, wd, inp.k, to_device(dout_bits), logits=to_device(inp.logits))
+    else:
+        T, k = inp.T, inp.k
+        res = tre.moe_backward(x, wgu, wd, k, to_device(dout_bits),
+                               topk_idx=to_device(inp.pair_expert.reshape(T, k)),
+                               topk_w=to_device(inp.pair_w.reshape(T, k)))
+    sync()
+    return {key: to_host(v) for key, v in res.items()}
+
+
+def check_backward(tre, inp, seed):
+    rng = np.random.default_rng(seed)
+    dout = workloads.bf16_bits(rng.normal(size=(inp.T, inp.d)).astype(np.float32))
+    got = run_backward(tre, inp, dout)
+    d64 = workloads.to_float32(dout).astype(np.float64)
+    if inp.logits is not None:
+        ref = oracle.backward(inp.x, inp.w_gate_up, inp.w_down, inp.k, d64, logits=inp.logits)
+        assert np.array_equal(got["topk_idx"], ref["idx"])
+    else:
+        ref = oracle.backward(inp.x, inp.w_gate_up, inp.w_down, inp.k, d64,
+                              pair_expert=inp.pair_expert, pair_w=inp.pair_w)
+    errs = {}
+    for key, rkey in (("dx", "dx"), ("dw_gate_up", "dw_gate_up"), ("dw_down", "dw_down"), ("dtopk_w", "dw"),
+                      ("dlogits", "dlogits")):
+        if rkey not in ref:
+            continue
+        r = ref[rkey]
+        if not np.any(r):
+            assert not np.any(as_f64(got[key])), key  # exact zeros stay zero
+            errs[key] = 0.0
+            continue
+        errs[key] = rel_l2(got[key], r)
+    say(f"  backward {inp.name} T={inp.T} d={inp.d} E={inp.E} k={inp.k} I={inp.I}: " +
+        ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for key, v in errs.items():
+        assert v <= TOL["bf16"], key
+    # experts that received no rows have exactly zero weight gradients
+    ids = ref["idx"].reshape(-1)
+    for e in range(inp.E):
+        if not np.any(ids == e):
+            assert not np.any(as_f64(got["dw_gate_up"][e])) and not np.any(as_f64(got["dw_down"][e])), e
+    return got, ref
+
+
+@pytest.mark.parametrize("T,d,E,k,I,logits", [
+    (300, 256, 8, 2, 320, "normal"),
+    (1000, 192, 7, 3, 320, "normal_bias"),   # ragged experts and column tiles
+    (64, 128, 16, 1, 128, "normal"),         # k = 1: no logit gradient
+    (5, 64, 256, 8, 64, "normal"),           # most experts empty, widest E
+    (4096, 512, 8, 2, 576, "normal_bias"),   # 256-row tiles, I not a multiple of 128
+])
+def test_backward_shapes(tre, T, d, E, k, I, logits):
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + E + 50, logits=logits)
+    got, _ = check_backward(tre, inp, seed=T)
+    if k == 1:
+        assert not np.any(got["dlogits"])
+
+
+def test_backward_given_pairs_with_masked(tre):
+    inp = workloads.make_custom(T=600, d=128, E=16, k=1, I=128, dtype="bf16", seed=63, logits=None,
+                                zero_experts=3)
+    inp.pair_expert[::9] = -1
+    got, _ = check_backward(tre, inp, seed=64)
+    assert np.all(got["dtopk_w"].reshape(-1)[::9] == 0)
+
+
+def test_backward_small_bf16(tre):
+    inp = workloads.make("small_bf16")
+    say("backward small_bf16 (full oracle)")
+    check_backward(tre, inp, seed=65)
+
+
+def test_backward_deterministic(tre):
+    inp = workloads.make_custom(T=512, d=256, E=8, k=2, I=256, dtype="bf16", seed=66, logits="normal")
+    dout = workloads.bf16_bits(np.random.default_rng(67).normal(size=(512, 256)).astype(np.float32))
+    a = run_backward(tre, inp, dout)
+    b = run_backward(tre, inp, dout)
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+def test_backward_empty_batch(tre):
+    torch = _torch()
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    wgu = torch.ones((4, 128, 256), dtype=torch.bfloat16, device="cuda")
+    wd = torch.ones((4, 128, 128), dtype=torch.bfloat16, device="cuda")
+    res = tre.moe_backward(x, wgu, wd, 2, torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda"),
+                           logits=torch.zeros((0, 4), dtype=torch.float32, device="cuda"))
+    sync()
+    assert not torch.any(res["dw_gate_up"].float()) and not torch.any(res["dw_down"].float())

@@ -70,6 +70,8 @@ def load(build_if_missing: bool = True):
         "moe_combine": ([p, i32, p, p, i32, i32, i32, st, p, p], st),
         "moe_forward_workspace_size": ([i32, i32, i32, i32, i32, st], sz),
         "moe_forward": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, sz, p], st),
+        "moe_backward_workspace_size": ([i32, i32, i32, i32, i32, st], sz),
+        "moe_backward": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, p, p, sz, p], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -328,3 +330,49 @@ def moe_forward(x, w_gate_up, w_down, k: int, logits=None, topk_idx=None, topk_w
                                           _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token),
                                           _ptr(pair_row), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
     return out, topk_idx, topk_w
+
+
+def moe_backward_workspace_size(T: int, d: int, E: int, k: int, I: int, dtype) -> int:
+    return int(load().moe_backward_workspace_size(T, d, E, k, I, dtype))
+
+
+def moe_backward(x, w_gate_up, w_down, k: int, dout, logits=None, topk_idx=None, topk_w=None,
+                 want_dlogits: bool = True, workspace=None, stream=None):
+    """Gradients of <dout, moe_forward(x, ...)> (bf16).  With ``logits`` the layer
+    routes first (topk_idx / topk_w are outputs, and dlogits is returned when
+    ``want_dlogits``); without, ``topk_idx`` / ``topk_w`` are the given pairs.
+    Returns a dict with dx, dw_gate_up, dw_down, dtopk_w, topk_idx, topk_w and
+    (with logits) dlogits."""
+    torch = _torch()
+    lib = load()
+    T, d = x.shape
+    E, d2, two_i = w_gate_up.shape
+    I = two_i // 2
+    if d2 != d or two_i != 2 * I:
+        raise ValueError(f"w_gate_up {tuple(w_gate_up.shape)} does not match d={d}")
+    _expect(w_gate_up, x.dtype, (E, d, 2 * I), "w_gate_up")
+    _expect(w_down, x.dtype, (E, I, d), "w_down")
+    _expect(dout, x.dtype, (T, d), "dout")
+    if logits is not None:
+        _expect(logits, torch.float32, (T, E), "logits")
+        topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
+        topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
+    elif topk_idx is None or topk_w is None:
+        raise ValueError("without logits, topk_idx and topk_w must be given")
+    _expect(topk_idx.reshape(T, k), torch.int32, (T, k), "topk_idx")
+    _expect(topk_w.reshape(T, k), torch.float32, (T, k), "topk_w")
+    dx = _empty((T, d), x.dtype, x)
+    dwgu = _empty((E, d, 2 * I), x.dtype, x)
+    dwd = _empty((E, I, d), x.dtype, x)
+    dtw = _empty((T, k), torch.float32, x)
+    dlg = _empty((T, E), torch.float32, x) if (logits is not None and want_dlogits) else None
+    dt = _dt(x)
+    nbytes = lib.moe_backward_workspace_size(T, d, E, k, I, dt)
+    ws = _workspace(nbytes, x, workspace)
+    _check("moe_backward", lib.moe_backward(_ptr(x), _ptr(logits), T, d, E, k, I, _ptr(w_gate_up), _ptr(w_down), dt,
+                                            _ptr(topk_idx), _ptr(topk_w), _ptr(dout), _ptr(dx), _ptr(dwgu),
+                                            _ptr(dwd), _ptr(dtw), _ptr(dlg), _ptr(ws), nbytes, _stream(stream)))
+    res = dict(dx=dx, dw_gate_up=dwgu, dw_down=dwd, dtopk_w=dtw, topk_idx=topk_idx, topk_w=topk_w)
+    if dlg is not None:
+        res["dlogits"] = dlg
+    return res

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "combine.hip", "wgrad.hip"]
 ARCH = "gfx950"
 
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",

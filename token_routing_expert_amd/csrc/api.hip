@@ -56,6 +56,31 @@ ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
   return L;
 }
 
+// Byte layout of the moe_backward workspace (bf16): the recomputed forward
+// intermediates and the row gradients, each 256-byte aligned.
+struct BackwardLayout {
+  size_t pair_row, row_token, offsets, perm_ws, x_perm, h, gu, y, dy, dgu, dxp, total;
+};
+
+BackwardLayout backward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
+  const int64_t P = T * k;
+  BackwardLayout L;
+  size_t o = 0;
+  L.pair_row = o;  o += align256(P * 4);
+  L.row_token = o; o += align256(P * 4);
+  L.offsets = o;   o += align256((E + 1) * 4);
+  L.perm_ws = o;   o += permute_index_workspace(P, (int)E);
+  L.x_perm = o;    o += align256(P * d * 2);
+  L.h = o;         o += align256(P * I * 2);
+  L.gu = o;        o += align256(P * 2 * I * 2);
+  L.y = o;         o += align256(P * d * 2);
+  L.dy = o;        o += align256(P * d * 2);
+  L.dgu = o;       o += align256(P * 2 * I * 2);
+  L.dxp = o;       o += align256(P * d * 2);
+  L.total = o;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,6 +287,72 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
   TRY(from_hip(launch_grouped_ffn_f32((const float*)x_perm, offs, P, E, d, I, (const float*)w_gate_up,
                                       (const float*)w_down, (float*)h, (float*)y_perm, s)));
   return from_hip(launch_combine_f32((const float*)y_perm, P, p_row, topk_w, T, k, d, (float*)out, s));
+}
+
+size_t moe_backward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, moe_dtype dt) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || I < 1 || dt != MOE_BF16) return 0;
+  return backward_layout(T, d, E, k, I).total;
+}
+
+moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
+                        const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
+                        const void* dout, void* dx, void* dw_gate_up, void* dw_down, float* dtopk_w, float* dlogits,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt) || T < 0 || k < 1) return MOE_ERR_ARG;
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  TRY(check_experts(E));
+  if (logits && k > E) return MOE_ERR_ARG;
+  if (dlogits && !logits) return MOE_ERR_ARG;
+  TRY(check_width(d));
+  TRY(check_width(I));
+  const int64_t P = (int64_t)T * k;
+  if (P * (d > 2 * I ? d : 2 * I) >= kMaxElems || (int64_t)T * E >= kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)E * d * 2 * I >= 8 * kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d * I * 4 >= kMaxElems) return MOE_ERR_UNSUPPORTED;   // one expert's weights < 2 GiB
+  if (T == 0) {
+    // no rows: every weight gradient is zero, and nothing else exists
+    if (E > 0 && (!dw_gate_up || !dw_down)) return MOE_ERR_ARG;
+    hipStream_t s0 = (hipStream_t)stream;
+    TRY(from_hip(launch_zero_bf16((bf16_t*)dw_gate_up, (int64_t)E * d * 2 * I, s0)));
+    return from_hip(launch_zero_bf16((bf16_t*)dw_down, (int64_t)E * I * d, s0));
+  }
+  if (!x || !w_gate_up || !w_down || !topk_idx || !topk_w || !dout || !dx || !dw_gate_up || !dw_down || !dtopk_w)
+    return MOE_ERR_ARG;
+  const BackwardLayout L = backward_layout(T, d, E, k, I);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  char* ws = (char*)workspace;
+  int32_t* p_row = (int32_t*)(ws + L.pair_row);
+  int32_t* r_tok = (int32_t*)(ws + L.row_token);
+  int32_t* offs = (int32_t*)(ws + L.offsets);
+  bf16_t* x_perm = (bf16_t*)(ws + L.x_perm);
+  bf16_t* h = (bf16_t*)(ws + L.h);
+  bf16_t* gu = (bf16_t*)(ws + L.gu);
+  bf16_t* y = (bf16_t*)(ws + L.y);
+  bf16_t* dy = (bf16_t*)(ws + L.dy);
+  bf16_t* dgu = (bf16_t*)(ws + L.dgu);
+  bf16_t* dxp = (bf16_t*)(ws + L.dxp);
+  const bf16_t* wgu = (const bf16_t*)w_gate_up;
+  const bf16_t* wd = (const bf16_t*)w_down;
+  hipStream_t s = (hipStream_t)stream;
+
+  // the forward again, keeping what the gradients need
+  if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
+  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s)));
+  TRY(from_hip(launch_move_rows(x, T, (int64_t)d * 2, r_tok, offs, E, P, x_perm, s)));
+  TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, wgu, h, gu, s)));
+  TRY(from_hip(launch_down_bf16(h, offs, P, E, d, I, wd, y, s)));
+  // combine -> routing weights (and logits) and the expert rows' gradient
+  TRY(from_hip(launch_combine_bwd_bf16((const bf16_t*)dout, y, P, p_row, topk_w, topk_idx, T, k, d, E, dy, dtopk_w,
+                                       dlogits, s)));
+  // down projection and SwiGLU
+  TRY(from_hip(launch_down_dgrad_swiglu_bf16(dy, offs, P, E, d, I, wd, gu, dgu, s)));
+  TRY(from_hip(launch_wgrad_bf16(h, I, I, dy, d, d, offs, P, E, (bf16_t*)dw_down, s)));
+  // gate/up projection
+  TRY(from_hip(launch_gate_up_dgrad_bf16(dgu, offs, P, E, d, I, wgu, dxp, s)));
+  TRY(from_hip(launch_wgrad_bf16(x_perm, d, d, dgu, 2 * I, 2 * I, offs, P, E, (bf16_t*)dw_gate_up, s)));
+  // each token's row gradients summed back in token order
+  return from_hip(launch_combine_bf16(dxp, P, p_row, nullptr, T, k, d, (bf16_t*)dx, s));
 }
 
 }  // extern "C"

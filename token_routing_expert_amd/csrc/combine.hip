@@ -73,13 +73,64 @@ __global__ __launch_bounds__(kThreads) void k_combine(const u32x4* __restrict__ 
     for (int j = 0; j < k; ++j) {
       const int64_t r = pair_row[t * k + j];
       if (r < 0 || r >= max_rows) continue;
-      const float w = pair_w[t * k + j];
+      const float w = pair_w ? pair_w[t * k + j] : 1.f;
       float f[n];
       Vec<Elem>::load(y[r * vec_per_row + v], f);
 #pragma unroll
       for (int i = 0; i < n; ++i) acc[i] = fmaf(w, f[i], acc[i]);
     }
     out[t * vec_per_row + v] = Vec<Elem>::store(acc);
+  }
+}
+
+// Backward of the combine (bf16).  With dy_p = w_p dout_t for pair p = (t, j):
+//   dy[pair_row[p]] = w_p * dout[t]          (the gradient reaching the expert)
+//   dw[p]           = <dout[t], y[pair_row[p]]>  (the routing weight's gradient)
+// and, when the weights are the softmax of the selected logits,
+//   dlogits[t, topk_idx[p]] = w_p (dw_p - sum_i w_i dw_i), zero elsewhere.
+// One wave per token, slots in ascending order; each dot product is summed
+// in float32 over the lanes' 16-byte vectors and then across the wave.
+__global__ __launch_bounds__(kThreads) void k_combine_bwd(
+    const u32x4* __restrict__ dout, const u32x4* __restrict__ y, int64_t max_rows, const int32_t* __restrict__ pair_row,
+    const float* __restrict__ pair_w, const int32_t* __restrict__ topk_idx, int64_t n_tok, int k, int E,
+    int64_t vec_per_row, u32x4* __restrict__ dy, float* __restrict__ dw, float* __restrict__ dlogits) {
+  // every lane of a wave writes the same value to its token's slot j and
+  // later reads back only what it wrote itself
+  __shared__ float s_dw[kThreads / kWave][kMaxExperts];
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= n_tok) return;
+  const int lane = threadIdx.x % kWave;
+  float* my_dw = s_dw[threadIdx.x / kWave];
+  float inner = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int64_t r = pair_row[t * k + j];
+    const bool live = r >= 0 && r < max_rows;
+    const float w = pair_w[t * k + j];
+    float dot = 0.f;
+    if (live) {
+      for (int64_t v = lane; v < vec_per_row; v += kWave) {
+        float g[8], f[8];
+        Vec<bf16_t>::load(dout[t * vec_per_row + v], g);
+        Vec<bf16_t>::load(y[r * vec_per_row + v], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf(g[i], f[i], dot);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] *= w;
+        dy[r * vec_per_row + v] = Vec<bf16_t>::store(g);
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, kWave);
+    }
+    if (lane == 0) dw[t * k + j] = dot;
+    my_dw[j] = dot;
+    inner = fmaf(w, dot, inner);
+  }
+  if (!dlogits) return;
+  for (int e = lane; e < E; e += kWave) {
+    float v = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (topk_idx[t * k + j] == e) v = pair_w[t * k + j] * (my_dw[j] - inner);
+    dlogits[t * E + e] = v;
   }
 }
 
@@ -98,6 +149,17 @@ hipError_t launch(const Elem* y, int64_t max_rows, const int32_t* pair_row, cons
 hipError_t launch_combine_bf16(const bf16_t* y_perm, int64_t max_rows, const int32_t* pair_row,
                                const float* pair_w, int64_t T, int k, int d, bf16_t* out, hipStream_t s) {
   return launch<bf16_t>(y_perm, max_rows, pair_row, pair_w, T, k, d, out, s);
+}
+
+hipError_t launch_combine_bwd_bf16(const bf16_t* dout, const bf16_t* y_perm, int64_t max_rows,
+                                  const int32_t* pair_row, const float* pair_w, const int32_t* topk_idx, int64_t T,
+                                  int k, int d, int E, bf16_t* dy_perm, float* dw, float* dlogits, hipStream_t s) {
+  const int64_t vec_per_row = (int64_t)d * 2 / 16;
+  const int64_t blocks = ceil_div(T, kThreads / kWave);
+  k_combine_bwd<<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)dout, (const u32x4*)y_perm, max_rows, pair_row,
+                                                     pair_w, topk_idx, T, k, E, vec_per_row, (u32x4*)dy_perm, dw,
+                                                     dlogits);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine_f32(const float* y_perm, int64_t max_rows, const int32_t* pair_row,

@@ -66,6 +66,19 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// MFMA operand (32 rows x 16 k, lane l: row l % 32, k 8 (l / 32) .. +7) from
+// an LDS tile stored k-row by k-row (rows of the operand contiguous): two
+// transposing 64-bit reads, at k-rows kr and kr + 4 of the lane's column.
+__device__ __forceinline__ bf16x8 lds_read_b_operand(const bf16_t* p0, const bf16_t* p1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Workgroup barrier that neither the scheduler nor the compiler's memory
 // model moves work across, and that does not drain outstanding LDS-writing
 // loads the way __syncthreads() does.
@@ -127,5 +140,29 @@ hipError_t launch_combine_bf16(const bf16_t* y_perm, int64_t max_rows, const int
 hipError_t launch_combine_f32(const float* y_perm, int64_t max_rows, const int32_t* pair_row,
                               const float* pair_w, int64_t T, int k, int d, float* out,
                               hipStream_t s);
+// (pair_w == nullptr: every weight is 1 -- the backward's sum of a token's row gradients)
+
+// ---- backward (bf16) ----
+// forward gate/up that also keeps the pre-activations: gu [max_rows, 2I] = [x Wg | x Wu]
+hipError_t launch_gate_up_save_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
+                                    int I, const bf16_t* w_gate_up, bf16_t* h, bf16_t* gu, hipStream_t s,
+                                    const int32_t* row_token = nullptr, int64_t x_rows = 0);
+// dy[pair_row[p]] = w_p dout[t]; dw[p] = <dout[t], y_perm[pair_row[p]]>; dlogits (when non-null) through
+// the renormalised softmax of the selected logits
+hipError_t launch_combine_bwd_bf16(const bf16_t* dout, const bf16_t* y_perm, int64_t max_rows,
+                                  const int32_t* pair_row, const float* pair_w, const int32_t* topk_idx, int64_t T,
+                                  int k, int d, int E, bf16_t* dy_perm, float* dw, float* dlogits, hipStream_t s);
+// dgu = [dg | du] from dh = dy Wd^T and the saved gu
+hipError_t launch_down_dgrad_swiglu_bf16(const bf16_t* dy, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                         int d, int I, const bf16_t* w_down, const bf16_t* gu, bf16_t* dgu,
+                                         hipStream_t s);
+// dx_perm = dgu Wgu^T
+hipError_t launch_gate_up_dgrad_bf16(const bf16_t* dgu, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                     int d, int I, const bf16_t* w_gate_up, bf16_t* dx_perm, hipStream_t s);
+// p[0, n) = 0 by a plain kernel (no memset node when captured in a graph); n % 8 == 0
+hipError_t launch_zero_bf16(bf16_t* p, int64_t n, hipStream_t s);
+// dW[e] [M, N] = sum over the rows r of expert e of a[r][:M]^T b[r][:N]
+hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, int M, const bf16_t* b, int ldb, int N,
+                             const int32_t* expert_offsets, int64_t max_rows, int E, bf16_t* dw, hipStream_t s);
 
 }  // namespace tre

@@ -44,15 +44,25 @@ constexpr int NTHR = 256;        // 4 waves per workgroup
 constexpr int kXcd = 8;          // XCDs per MI355X; workgroups are dealt round-robin over them
 // byte offset that is always past num_records (a buffer load there returns zeros)
 constexpr uint32_t kOutOfRange = 0x80000000u;
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ bf16x8 lds_read_b_operand(const bf16_t* p0, const bf16_t* p1) {
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
+// epilogues of the grouped GEMM
+constexpr int kEpiPlain = 0;       // Out = A W
+constexpr int kEpiSwiglu = 1;      // Out = silu(A Wg) * (A Wu) (gate/up tiles)
+constexpr int kEpiSwigluSave = 2;  // as kEpiSwiglu, and Out2 = [A Wg | A Wu] (row stride 2N)
+constexpr int kEpiSwigluBwd = 3;   // Out = [dg | du] from dh = A W and Aux = [g | u] (row strides 2N)
+
+__device__ __forceinline__ uint2 pack4(const float* f) {
+  return make_uint2((uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16),
+                    (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16));
 }
+
+__device__ __forceinline__ void unpack4(uint2 v, float* f) {
+  f[0] = __builtin_bit_cast(float, v.x << 16);
+  f[1] = __builtin_bit_cast(float, v.x & 0xFFFF0000u);
+  f[2] = __builtin_bit_cast(float, v.y << 16);
+  f[3] = __builtin_bit_cast(float, v.y & 0xFFFF0000u);
+}
+
 
 template <int NWAVES>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
@@ -154,11 +164,14 @@ __device__ __forceinline__ void wait_for_stage(int64_t after) {
 // and its epilogue.  With row_token, the grouped-row -> token map of the
 // next tile is fetched into LDS by DMA one tile ahead, so that entering a
 // tile never waits on a plain global load (which would drain the ring).
-template <bool SWIGLU, int BK, int OCC, int NJ, int WM, int NS, bool PP>
+template <int EPI, bool BT, int BK, int OCC, int NJ, int WM, int NS, bool PP>
 __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K, int N, int ldw,
     const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles, const int32_t* __restrict__ row_token,
-    int64_t a_rows) {
+    int64_t a_rows, bf16_t* __restrict__ Out2, const bf16_t* __restrict__ Aux) {
+  // gate/up tiles: 128 gate columns and the matching 128 up columns
+  constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
+  static_assert(!(SWIGLU && BT), "the gate/up weight is only read as [K][2N]");
   typedef Geo<BK, NJ, WM> GE;
   constexpr int BM = GE::BM, WAVES = GE::WAVES;
   constexpr int BNB = GE::BNB;
@@ -259,7 +272,10 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     a_rsrc = row_token ? __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(a_rows * K * 2), kBufferConfig)
                        : __builtin_amdgcn_make_buffer_rsrc((void*)(A + t.row0 * K), (short)0, t.rows * K * 2,
                                                            kBufferConfig);
-    b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)t.e * K * ldw), (short)0, K * ldw * 2,
+    // one expert's weights: [K][ldw] (read transposed by the LDS reads), or
+    // with BT [N][K] (rows of k, read like the activations)
+    const int64_t w_elems = BT ? (int64_t)N * K : (int64_t)K * ldw;
+    b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)t.e * w_elems), (short)0, (int)(w_elems * 2),
                                                kBufferConfig);
 #pragma unroll
     for (int p = 0; p < GE::A_INSTR; ++p) {
@@ -273,6 +289,14 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     }
 #pragma unroll
     for (int p = 0; p < GE::B_INSTR; ++p) {
+      if constexpr (BT) {
+        // weight row n of the tile holds its BK k-values like an activation row
+        const int nr = (wave + WAVES * p) * GE::RPI + lane / GE::CPR;
+        const int c = (lane % GE::CPR) ^ GE::swz(nr);
+        const int gn = t.n0 + nr;
+        b_voff[p] = gn < N ? (uint32_t)((int64_t)gn * K + c * 8) * 2u : kOutOfRange;
+        continue;
+      }
       const int kr = (wave + WAVES * p) * GE::BRPI + lane / GE::BCPR;
       const int c = (lane % GE::BCPR) ^ ((kr & 3) << 2);
       const int tc = c * 8;
@@ -297,7 +321,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   auto issue_next = [&](int buf) {
     if (i_k == 0) enter();
     const uint32_t ka = (uint32_t)i_k * BK * 2u;
-    const uint32_t kb = (uint32_t)i_k * BK * ldw * 2u;
+    const uint32_t kb = BT ? (uint32_t)i_k * BK * 2u : (uint32_t)i_k * BK * ldw * 2u;
     const uint32_t a_lds = lds_address(sA + buf * GE::A_BYTES) + wave * 1024;
     const uint32_t b_lds = lds_address(sB + buf * GE::B_BYTES) + wave * 1024;
 #pragma unroll
@@ -332,6 +356,10 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+      if constexpr (BT) {
+        f.b[j] = *(const bf16x8*)(b_buf + GE::a_byte(col_base(j) + lane % 32, ks * 2 + lane / 32));
+        continue;
+      }
       const int kr = ks * 16 + (g16 / 2) * 8 + L / 4;
       const int col = col_base(j) + (g16 % 2) * 16 + 4 * (L % 4);
       const uint32_t off = GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
@@ -374,6 +402,42 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
               packed[h2] = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
             }
             *(uint2*)(orow + c) = make_uint2(packed[0], packed[1]);
+            if constexpr (EPI == kEpiSwigluSave) {
+              // the pre-activations too: gate at column c, up at column N + c
+              bf16_t* srow = Out2 + (t.row0 + r) * 2 * N;
+              float gq[4], uq[4];
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                gq[v] = acc[j][i][4 * q4 + v];
+                uq[v] = acc[j + NJ / 2][i][4 * q4 + v];
+              }
+              *(uint2*)(srow + c) = pack4(gq);
+              *(uint2*)(srow + N + c) = pack4(uq);
+            }
+          }
+      } else if constexpr (EPI == kEpiSwigluBwd) {
+        // acc is dh; with the saved pre-activations g, u of the row:
+        // dg = dh u s (1 + g (1 - s)), du = dh g s, s = sigmoid(g)
+        const bf16_t* grow = Aux + (t.row0 + r) * 2 * N;
+        bf16_t* drow = Out + (t.row0 + r) * 2 * N;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int c = t.n0 + WCOL * wn + 32 * j + 8 * q4 + lc;
+            if (c >= N) continue;
+            float g[4], u[4], dg[4], du[4];
+            unpack4(*(const uint2*)(grow + c), g);
+            unpack4(*(const uint2*)(grow + N + c), u);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float dh = acc[j][i][4 * q4 + v];
+              const float sg = 1.f / (1.f + __expf(-g[v]));
+              dg[v] = dh * u[v] * sg * (1.f + g[v] * (1.f - sg));
+              du[v] = dh * g[v] * sg;
+            }
+            *(uint2*)(drow + c) = pack4(dg);
+            *(uint2*)(drow + N + c) = pack4(du);
           }
       } else {
 #pragma unroll
@@ -552,17 +616,25 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float* __restrict__ 
   y[r * d + c] = acc;
 }
 
-template <bool SWIGLU, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2, int NS = 3, bool PP = false>
+template <int EPI, bool BT = false, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2, int NS = 3, bool PP = false>
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
-                      int64_t a_rows = 0) {
+                      int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr) {
+  constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   constexpr int BNO = SWIGLU ? 32 * NJ : 64 * NJ;   // output columns per tile
   if (K / BK < NS - 1) return hipErrorInvalidValue;  // each tile spans at least NS - 1 stages
   const int nt = (int)ceil_div(N, BNO);
-  dma::k_grouped_gemm<SWIGLU, BK, OCC, NJ, WM, NS, PP><<<persistent_grid(max_rows, E, 64 * WM, nt, OCC), 128 * WM, 0, s>>>(
-      a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows);
+  dma::k_grouped_gemm<EPI, BT, BK, OCC, NJ, WM, NS, PP>
+      <<<persistent_grid(max_rows, E, 64 * WM, nt, OCC), 128 * WM, 0, s>>>(a, offsets, max_rows, E, K, N, ldw, w, out,
+                                                                          nt, row_token, a_rows, out2, aux);
   return hipGetLastError();
 }
+
+// One grouped product in the tile shape big_tiles picks.
+template <int EPI, bool BT>
+hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
+                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
+                       int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr);
 
 // 256-row tiles (8 waves in ping-pong, one workgroup per CU: each weight
 // stage feeds twice the rows) once the experts hold 128 rows or more on
@@ -570,22 +642,49 @@ hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows,
 // per CU) below that.
 bool big_tiles(int64_t max_rows, int E, int K) { return max_rows >= 128 * (int64_t)E && K >= 96; }
 
+template <int EPI, bool BT>
+hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
+                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token, int64_t a_rows,
+                       bf16_t* out2, const bf16_t* aux) {
+  if (big_tiles(max_rows, E, K))
+    return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
+                                                     a_rows, out2, aux);
+  return launch_dma<EPI, BT>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token, a_rows, out2, aux);
+}
+
 }  // namespace
 
 hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s, const int32_t* row_token,
                                int64_t x_rows) {
-  if (big_tiles(max_rows, E, d))
-    return launch_dma<true, 32, 1, 4, 4, 4, true>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s,
-                                                  row_token, x_rows);
-  return launch_dma<true>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token, x_rows);
+  return launch_auto<kEpiSwiglu, false>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token,
+                                        x_rows);
 }
 
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s) {
-  if (big_tiles(max_rows, E, I))
-    return launch_dma<false, 32, 1, 4, 4, 4, true>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
-  return launch_dma<false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
+  return launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
+}
+
+hipError_t launch_gate_up_save_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
+                                    int I, const bf16_t* w_gate_up, bf16_t* h, bf16_t* gu, hipStream_t s,
+                                    const int32_t* row_token, int64_t x_rows) {
+  return launch_auto<kEpiSwigluSave, false>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token,
+                                            x_rows, gu);
+}
+
+hipError_t launch_down_dgrad_swiglu_bf16(const bf16_t* dy, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                         int d, int I, const bf16_t* w_down, const bf16_t* gu, bf16_t* dgu,
+                                         hipStream_t s) {
+  // dh = dy Wd^T: Wd [I][d] is the [N][K] weight of a product with K = d, N = I
+  return launch_auto<kEpiSwigluBwd, true>(dy, expert_offsets, max_rows, E, d, I, d, w_down, dgu, s, nullptr, 0,
+                                          nullptr, gu);
+}
+
+hipError_t launch_gate_up_dgrad_bf16(const bf16_t* dgu, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                     int d, int I, const bf16_t* w_gate_up, bf16_t* dx_perm, hipStream_t s) {
+  // dx = [dg | du] Wgu^T: Wgu [d][2I] is the [N][K] weight of a product with K = 2I, N = d
+  return launch_auto<kEpiPlain, true>(dgu, expert_offsets, max_rows, E, 2 * I, d, 2 * I, w_gate_up, dx_perm, s);
 }
 
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
