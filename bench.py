@@ -65,6 +65,10 @@ def read_traffic_record(workload: str):
     return rec if "hbm_bytes_per_launch" in rec else None
 
 
+def inp_seed(name: str) -> int:
+    return int(workloads.CONFIGS[name]["seed"])
+
+
 def to_device(a, torch):
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
@@ -308,6 +312,47 @@ def main() -> int:
                   "hbm_frac": round(r_bytes / (r_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                   "tflops": round(r_flops / (r_ms * 1e-3) / 1e12, 2)}
 
+    # ---- timed region 4 (reported beside the layer): the layer's backward
+    # pass, moe_backward, which recomputes the forward it needs ----
+    backward = None
+    if inp.dtype == "bf16":
+        rng = np.random.default_rng([inp_seed(args.workload), 99])
+        dout = to_device(workloads.bf16_bits(rng.normal(size=(T, d)).astype(np.float32)), torch)
+        gdx = torch.empty((T, d), dtype=dev_dtype, device="cuda")
+        gwgu = torch.empty((E, d, 2 * I), dtype=dev_dtype, device="cuda")
+        gwd = torch.empty((E, I, d), dtype=dev_dtype, device="cuda")
+        gtw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        glg = torch.empty((T, E), dtype=torch.float32, device="cuda") if logits is not None else None
+        b_idx = torch.empty((T, k), dtype=torch.int32, device="cuda") if logits is not None else topk_idx
+        b_w = torch.empty((T, k), dtype=torch.float32, device="cuda") if logits is not None else topk_w
+        bws_bytes = lib.moe_backward_workspace_size(T, d, E, k, I, dt)
+        bws = torch.empty(max(bws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+        def run_backward():
+            st = lib.moe_backward(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(b_idx), ptr(b_w),
+                                  ptr(dout), ptr(gdx), ptr(gwgu), ptr(gwd), ptr(gtw), ptr(glg), ptr(bws), bws_bytes,
+                                  sp)
+            if st != 0:
+                raise RuntimeError(f"moe_backward failed with status {st}")
+        for _ in range(args.warmup):
+            run_backward()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for _ in range(args.steps):
+            run_backward()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        b_ms = b0.elapsed_time(b1) / args.steps
+        # matrix products per call: the recomputed forward (6 n d I) and the
+        # gradients (dh 2, dW_down 2, dx 4, dW_gate_up 4: 12 n d I)
+        b_flops = 18 * n_rows * d * I
+        backward = {"ms": round(b_ms, 5), "flops_per_call": b_flops,
+                    "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(b_flops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "pairs_per_s": P / (b_ms * 1e-3)}
+        del gdx, gwgu, gwd, bws
+
     work = algorithmic_work(inp, n_rows, live)
     peak_mm = PEAK_F32_TFLOPS if inp.dtype == "f32" else PEAK_BF16_TFLOPS
     kernels = {}
@@ -363,6 +408,7 @@ def main() -> int:
         "graph_ms_per_step": graph_ms,
         "permute_gbs": kernels["permute"].get("gbs"),
         "router_projection": router,
+        "backward": backward,
     }
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
