@@ -397,7 +397,9 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
 #pragma unroll
               for (int u = 0; u < 2; ++u) {
                 const float gt = acc[j][i][4 * q4 + 2 * h2 + u], up = acc[j + NJ / 2][i][4 * q4 + 2 * h2 + u];
-                hv[u] = gt / (1.f + __expf(-gt)) * up;
+                // silu(g) = g / (1 + e^-g), with the hardware reciprocal
+                // (about 1 ulp in float32, far below the bf16 rounding of h)
+                hv[u] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
               }
               packed[h2] = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
             }
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const float dh = acc[j][i][4 * q4 + v];
-              const float sg = 1.f / (1.f + __expf(-g[v]));
+              const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g[v]));
               dg[v] = dh * u[v] * sg * (1.f + g[v] * (1.f - sg));
               du[v] = dh * g[v] * sg;
             }
