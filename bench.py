@@ -328,30 +328,53 @@ def main() -> int:
         bws_bytes = lib.moe_backward_workspace_size(T, d, E, k, I, dt)
         bws = torch.empty(max(bws_bytes, 1), dtype=torch.uint8, device="cuda")
 
-        def run_backward():
+        def run_backward(recompute=1):
             st = lib.moe_backward(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(b_idx), ptr(b_w),
-                                  ptr(dout), ptr(gdx), ptr(gwgu), ptr(gwd), ptr(gtw), ptr(glg), ptr(bws), bws_bytes,
-                                  sp)
+                                  ptr(dout), ptr(gdx), ptr(gwgu), ptr(gwd), ptr(gtw), ptr(glg), recompute, ptr(bws),
+                                  bws_bytes, sp)
             if st != 0:
                 raise RuntimeError(f"moe_backward failed with status {st}")
+
+        def run_forward_train():
+            st = lib.moe_forward_train(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(b_idx),
+                                       ptr(b_w), ptr(gout), ptr(bws), bws_bytes, sp)
+            if st != 0:
+                raise RuntimeError(f"moe_forward_train failed with status {st}")
+        gout = torch.empty((T, d), dtype=dev_dtype, device="cuda")
+
+        def timed(fn, n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
         for _ in range(args.warmup):
             run_backward()
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        b0.record(stream)
-        for _ in range(args.steps):
-            run_backward()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        b_ms = b0.elapsed_time(b1) / args.steps
+        b_ms = timed(run_backward, args.steps)
+        # a training step: the forward that keeps its intermediates, then the
+        # backward from them (events around the pair, and around each)
+        for _ in range(args.warmup):
+            run_forward_train()
+            run_backward(0)
+        step_ms = timed(lambda: (run_forward_train(), run_backward(0)), args.steps)
+        ft_ms = timed(run_forward_train, args.steps)
+        bs_ms = timed(lambda: run_backward(0), args.steps)
         # matrix products per call: the recomputed forward (6 n d I) and the
         # gradients (dh 2, dW_down 2, dx 4, dW_gate_up 4: 12 n d I)
         b_flops = 18 * n_rows * d * I
         backward = {"ms": round(b_ms, 5), "flops_per_call": b_flops,
                     "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 1),
                     "mfma_frac": round(b_flops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                    "pairs_per_s": P / (b_ms * 1e-3)}
-        del gdx, gwgu, gwd, bws
+                    "pairs_per_s": P / (b_ms * 1e-3),
+                    # training step: 6 n d I (forward) + 12 n d I (gradients), no recompute
+                    "training_step": {"ms": round(step_ms, 5), "forward_train_ms": round(ft_ms, 5),
+                                      "backward_saved_ms": round(bs_ms, 5),
+                                      "tflops": round(18 * n_rows * d * I / (step_ms * 1e-3) / 1e12, 1),
+                                      "pairs_per_s": P / (step_ms * 1e-3)}}
+        del gdx, gwgu, gwd, bws, gout
 
     work = algorithmic_work(inp, n_rows, live)
     peak_mm = PEAK_F32_TFLOPS if inp.dtype == "f32" else PEAK_BF16_TFLOPS

@@ -190,8 +190,11 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
  *     dW_gate_up[e] = sum_p x_t^T [dg | du];  dx_t = sum_j [dg | du] Wgu[e]^T
  *     with logits: dlogits[t, e_j] = w_j (dtopk_w_j - sum_i w_i dtopk_w_i),
  *     zero for experts not selected (the selection passes no gradient).
- * The forward is recomputed inside (routing when logits are given, the
- * grouping, both projections).  bf16 only: bf16 operands and stored
+ * recompute = 1: the forward is recomputed inside (routing when logits are
+ * given, the grouping, both projections).  recompute = 0: the workspace
+ * holds what moe_forward_train left there for these same arguments (and
+ * topk_idx / topk_w are the arrays that call filled or read), untouched since;
+ * only the gradients are computed.  bf16 only: bf16 operands and stored
  * intermediates (the pre-activations g, u, h, y and the row gradients),
  * float32 accumulation, gradients rounded to bf16 (dtopk_w, dlogits float32).
  *   x, dout [T, d] bf16; w_gate_up [E, d, 2I], w_down [E, I, d] bf16
@@ -202,13 +205,27 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
  *     dlogits [T, E] float32 (output; NULL to skip; only with logits)
  *   workspace >= moe_backward_workspace_size(T, d, E, k, I, dt) bytes
  * Errors: as moe_forward; MOE_ERR_UNSUPPORTED for dt = MOE_F32; MOE_ERR_ARG
- * for dlogits without logits.  T == 0 zeroes the weight gradients only.    */
+ * for dlogits without logits or recompute not 0 or 1.  T == 0 zeroes the
+ * weight gradients only.                                                    */
 size_t moe_backward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, moe_dtype dt);
 moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
                         int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt,
                         int32_t* topk_idx, float* topk_w, const void* dout, void* dx, void* dw_gate_up,
-                        void* dw_down, float* dtopk_w, float* dlogits, void* workspace,
+                        void* dw_down, float* dtopk_w, float* dlogits, int32_t recompute, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* The forward of a training step: out exactly as moe_forward computes it
+ * (same kernels, same order of every sum), and the intermediates the
+ * backward needs -- the routing, the grouping, the grouped rows of x, the
+ * pre-activations g | u, h and the expert outputs y -- kept in the workspace
+ * for moe_backward(..., recompute = 0, same workspace).  bf16 only.
+ *   arguments as moe_forward (the expert_offsets / row_token / pair_row
+ *   outputs live in the workspace);
+ *   workspace >= moe_backward_workspace_size(T, d, E, k, I, dt) bytes        */
+moe_status moe_forward_train(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                             int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt,
+                             int32_t* topk_idx, float* topk_w, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

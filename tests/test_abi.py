@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(lib):
         "moe_status_string", "moe_route_topk", "moe_permute_workspace_size", "moe_permute",
         "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
         "moe_forward_workspace_size", "moe_forward", "moe_gate_up_swiglu", "moe_down_proj", "moe_route_project",
-        "moe_backward_workspace_size", "moe_backward"}
+        "moe_backward_workspace_size", "moe_backward", "moe_forward_train"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -131,9 +131,9 @@ def test_backward_validation(lib):
     f = lib.moe_backward
 
     def call(x=FAKE, logits=FAKE, T=10, d=128, E=8, k=2, I=64, dt=1, dout=FAKE, dlogits=FAKE, ws=FAKE,
-             ws_bytes=0):
+             ws_bytes=0, recompute=1):
         return f(x, logits, T, d, E, k, I, FAKE, FAKE, dt, FAKE, FAKE, dout, FAKE, FAKE, FAKE, FAKE, dlogits,
-                 ws, ws_bytes, None)
+                 recompute, ws, ws_bytes, None)
     assert call(dt=0) == 2                    # float32: not supported
     assert call(dt=5) == 1                    # bad dtype
     assert call(k=9) == 1                     # k > E with logits
@@ -144,6 +144,7 @@ def test_backward_validation(lib):
     assert call(dout=None) == 1               # NULL upstream gradient
     assert call(x=None) == 1
     assert call(ws_bytes=1024) == 3           # workspace too small
+    assert call(recompute=2) == 1             # recompute is 0 or 1
     need = lib.moe_backward_workspace_size(10, 128, 8, 2, 64, 1)
     assert call(ws=None, ws_bytes=need) == 3  # no workspace
     assert lib.moe_backward_workspace_size(10, 128, 8, 2, 64, 0) == 0
@@ -154,3 +155,16 @@ def test_backward_validation(lib):
 def test_weight_size_limit(lib):
     # one expert's gate/up weight 4*d*I bytes must stay below 2 GiB
     assert lib.moe_down_proj(FAKE, FAKE, 100, 2, 32768, 16384, FAKE, 1, FAKE, None) == 2
+
+
+def test_forward_train_validation(lib):
+    f = lib.moe_forward_train
+
+    def call(x=FAKE, logits=FAKE, T=10, d=128, E=8, k=2, I=64, dt=1, out=FAKE, ws=FAKE, ws_bytes=0):
+        return f(x, logits, T, d, E, k, I, FAKE, FAKE, dt, FAKE, FAKE, out, ws, ws_bytes, None)
+    assert call(dt=0) == 2                    # float32: not supported
+    assert call(k=9) == 1                     # k > E with logits
+    assert call(d=96) == 2                    # d % 64
+    assert call(out=None) == 1
+    assert call(ws_bytes=64) == 3             # needs the backward-sized workspace
+    assert call(T=0, x=None, out=None) == 0   # empty batch

@@ -657,3 +657,44 @@ def test_backward_empty_batch(tre):
                            logits=torch.zeros((0, 4), dtype=torch.float32, device="cuda"))
     sync()
     assert not torch.any(res["dw_gate_up"].float()) and not torch.any(res["dw_down"].float())
+
+
+@pytest.mark.parametrize("T,d,E,k,I,logits", [
+    (300, 256, 8, 2, 320, "normal"),
+    (4096, 512, 8, 2, 576, "normal_bias"),   # 256-row tiles
+    (600, 128, 16, 1, 128, None),            # given pairs, some masked
+])
+def test_training_step_saved_equals_recompute(tre, T, d, E, k, I, logits):
+    # the training forward's output equals moe_forward's bit for bit, and the
+    # backward from its saved state equals the recomputing backward bit for bit
+    torch = _torch()
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + 70, logits=logits,
+                                zero_experts=3 if logits is None else 0)
+    if logits is None:
+        inp.pair_expert[::7] = -1
+    x, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
+    dout = to_device(workloads.bf16_bits(np.random.default_rng(T).normal(size=(T, d)).astype(np.float32)))
+    if logits is not None:
+        lg = to_device(inp.logits)
+        ref_out, ref_idx, ref_w = tre.moe_forward(x, wgu, wd, k, logits=lg)
+        out, idx, w, ws = tre.moe_forward_train(x, wgu, wd, k, logits=lg)
+        g_re = tre.moe_backward(x, wgu, wd, k, dout, logits=lg)
+        g_sv = tre.moe_backward(x, wgu, wd, k, dout, logits=lg, topk_idx=idx, topk_w=w, workspace=ws,
+                                recompute=False)
+    else:
+        pi = to_device(inp.pair_expert.reshape(T, k))
+        pw = to_device(inp.pair_w.reshape(T, k))
+        ref_out, ref_idx, ref_w = tre.moe_forward(x, wgu, wd, k, topk_idx=pi, topk_w=pw)
+        out, idx, w, ws = tre.moe_forward_train(x, wgu, wd, k, topk_idx=pi, topk_w=pw)
+        g_re = tre.moe_backward(x, wgu, wd, k, dout, topk_idx=pi, topk_w=pw)
+        g_sv = tre.moe_backward(x, wgu, wd, k, dout, topk_idx=idx, topk_w=w, workspace=ws, recompute=False)
+    sync()
+    assert np.array_equal(to_host(out).view(np.uint16), to_host(ref_out).view(np.uint16))
+    assert np.array_equal(to_host(idx), to_host(ref_idx))
+    for key in g_re:
+        assert np.array_equal(to_host(g_re[key]).view(np.uint8), to_host(g_sv[key]).view(np.uint8)), key
+    # and the saved-state gradients meet the oracle
+    ref = oracle.backward(inp.x, inp.w_gate_up, inp.w_down, k, workloads.to_float32(to_host(dout)).astype(np.float64),
+                          logits=inp.logits, pair_expert=inp.pair_expert, pair_w=inp.pair_w)
+    for key, rkey in (("dx", "dx"), ("dw_gate_up", "dw_gate_up"), ("dw_down", "dw_down"), ("dtopk_w", "dw")):
+        assert rel_l2(to_host(g_sv[key]), ref[rkey]) <= TOL["bf16"], key

@@ -71,7 +71,8 @@ def load(build_if_missing: bool = True):
         "moe_forward_workspace_size": ([i32, i32, i32, i32, i32, st], sz),
         "moe_forward": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, sz, p], st),
         "moe_backward_workspace_size": ([i32, i32, i32, i32, i32, st], sz),
-        "moe_backward": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, p, p, sz, p], st),
+        "moe_backward": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, p, i32, p, sz, p], st),
+        "moe_forward_train": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, sz, p], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -336,13 +337,51 @@ def moe_backward_workspace_size(T: int, d: int, E: int, k: int, I: int, dtype) -
     return int(load().moe_backward_workspace_size(T, d, E, k, I, dtype))
 
 
+def moe_forward_train(x, w_gate_up, w_down, k: int, logits=None, topk_idx=None, topk_w=None, out=None,
+                      workspace=None, stream=None):
+    """The forward of a training step (bf16): ``out`` as moe_forward computes it, and
+    the intermediates the backward needs kept in ``workspace`` (a backward-sized
+    buffer, allocated when None).  Returns (out, topk_idx, topk_w, workspace); pass
+    the same topk arrays and workspace to ``moe_backward(..., recompute=False)``."""
+    torch = _torch()
+    lib = load()
+    T, d = x.shape
+    E, d2, two_i = w_gate_up.shape
+    I = two_i // 2
+    if d2 != d or two_i != 2 * I:
+        raise ValueError(f"w_gate_up {tuple(w_gate_up.shape)} does not match d={d}")
+    _expect(w_gate_up, x.dtype, (E, d, 2 * I), "w_gate_up")
+    _expect(w_down, x.dtype, (E, I, d), "w_down")
+    if logits is not None:
+        _expect(logits, torch.float32, (T, E), "logits")
+        topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
+        topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
+    elif topk_idx is None or topk_w is None:
+        raise ValueError("without logits, topk_idx and topk_w must be given")
+    _expect(topk_idx.reshape(T, k), torch.int32, (T, k), "topk_idx")
+    _expect(topk_w.reshape(T, k), torch.float32, (T, k), "topk_w")
+    out = _empty((T, d), x.dtype, x) if out is None else out
+    _expect(out, x.dtype, (T, d), "out")
+    dt = _dt(x)
+    nbytes = lib.moe_backward_workspace_size(T, d, E, k, I, dt)
+    ws = _workspace(nbytes, x, workspace)
+    _check("moe_forward_train", lib.moe_forward_train(_ptr(x), _ptr(logits), T, d, E, k, I, _ptr(w_gate_up),
+                                                      _ptr(w_down), dt, _ptr(topk_idx), _ptr(topk_w), _ptr(out),
+                                                      _ptr(ws), nbytes, _stream(stream)))
+    return out, topk_idx, topk_w, ws
+
+
 def moe_backward(x, w_gate_up, w_down, k: int, dout, logits=None, topk_idx=None, topk_w=None,
-                 want_dlogits: bool = True, workspace=None, stream=None):
+                 want_dlogits: bool = True, workspace=None, recompute: bool = True, stream=None):
     """Gradients of <dout, moe_forward(x, ...)> (bf16).  With ``logits`` the layer
     routes first (topk_idx / topk_w are outputs, and dlogits is returned when
     ``want_dlogits``); without, ``topk_idx`` / ``topk_w`` are the given pairs.
+    ``recompute=False`` uses what moe_forward_train left in ``workspace`` (pass its
+    topk arrays too) instead of recomputing the forward.
     Returns a dict with dx, dw_gate_up, dw_down, dtopk_w, topk_idx, topk_w and
     (with logits) dlogits."""
+    if not recompute and (workspace is None or topk_idx is None or topk_w is None):
+        raise ValueError("recompute=False needs the workspace and topk arrays of moe_forward_train")
     torch = _torch()
     lib = load()
     T, d = x.shape
@@ -371,7 +410,8 @@ def moe_backward(x, w_gate_up, w_down, k: int, dout, logits=None, topk_idx=None,
     ws = _workspace(nbytes, x, workspace)
     _check("moe_backward", lib.moe_backward(_ptr(x), _ptr(logits), T, d, E, k, I, _ptr(w_gate_up), _ptr(w_down), dt,
                                             _ptr(topk_idx), _ptr(topk_w), _ptr(dout), _ptr(dx), _ptr(dwgu),
-                                            _ptr(dwd), _ptr(dtw), _ptr(dlg), _ptr(ws), nbytes, _stream(stream)))
+                                            _ptr(dwd), _ptr(dtw), _ptr(dlg), 1 if recompute else 0, _ptr(ws),
+                                            nbytes, _stream(stream)))
     res = dict(dx=dx, dw_gate_up=dwgu, dw_down=dwd, dtopk_w=dtw, topk_idx=topk_idx, topk_w=topk_w)
     if dlg is not None:
         res["dlogits"] = dlg

@@ -294,21 +294,69 @@ size_t moe_backward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, i
   return backward_layout(T, d, E, k, I).total;
 }
 
-moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
-                        const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
-                        const void* dout, void* dx, void* dw_gate_up, void* dw_down, float* dtopk_w, float* dlogits,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Validation shared by the training forward and the backward (bf16 only).
+moe_status check_train(moe_dtype dt, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, const float* logits) {
   if (!dtype_ok(dt) || T < 0 || k < 1) return MOE_ERR_ARG;
   if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   TRY(check_experts(E));
   if (logits && k > E) return MOE_ERR_ARG;
-  if (dlogits && !logits) return MOE_ERR_ARG;
   TRY(check_width(d));
   TRY(check_width(I));
   const int64_t P = (int64_t)T * k;
   if (P * (d > 2 * I ? d : 2 * I) >= kMaxElems || (int64_t)T * E >= kMaxElems) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)E * d * 2 * I >= 8 * kMaxElems) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d * I * 4 >= kMaxElems) return MOE_ERR_UNSUPPORTED;   // one expert's weights < 2 GiB
+  return MOE_OK;
+}
+
+// The forward with everything the gradients need kept in a backward-layout
+// workspace: routing (with logits), grouping, the grouped copy of x, the
+// pre-activations g | u, h and the expert outputs y.
+moe_status forward_keep(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
+                        const void* w_gate_up, const void* w_down, int32_t* topk_idx, float* topk_w,
+                        const BackwardLayout& L, char* ws, hipStream_t s) {
+  const int64_t P = (int64_t)T * k;
+  int32_t* p_row = (int32_t*)(ws + L.pair_row);
+  int32_t* r_tok = (int32_t*)(ws + L.row_token);
+  int32_t* offs = (int32_t*)(ws + L.offsets);
+  bf16_t* x_perm = (bf16_t*)(ws + L.x_perm);
+  bf16_t* h = (bf16_t*)(ws + L.h);
+  bf16_t* gu = (bf16_t*)(ws + L.gu);
+  bf16_t* y = (bf16_t*)(ws + L.y);
+  if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
+  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s)));
+  TRY(from_hip(launch_move_rows(x, T, (int64_t)d * 2, r_tok, offs, E, P, x_perm, s)));
+  TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up, h, gu, s)));
+  return from_hip(launch_down_bf16(h, offs, P, E, d, I, (const bf16_t*)w_down, y, s));
+}
+
+}  // namespace
+
+moe_status moe_forward_train(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                             int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx,
+                             float* topk_w, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_train(dt, T, d, E, k, I, logits));
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate_up || !w_down || !topk_idx || !topk_w || !out) return MOE_ERR_ARG;
+  const BackwardLayout L = backward_layout(T, d, E, k, I);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  TRY(forward_keep(x, logits, T, d, E, k, I, w_gate_up, w_down, topk_idx, topk_w, L, ws, s));
+  return from_hip(launch_combine_bf16((const bf16_t*)(ws + L.y), (int64_t)T * k, (const int32_t*)(ws + L.pair_row),
+                                      topk_w, T, k, d, (bf16_t*)out, s));
+}
+
+moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
+                        const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
+                        const void* dout, void* dx, void* dw_gate_up, void* dw_down, float* dtopk_w, float* dlogits,
+                        int32_t recompute, void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_train(dt, T, d, E, k, I, logits));
+  if (dlogits && !logits) return MOE_ERR_ARG;
+  if (recompute != 0 && recompute != 1) return MOE_ERR_ARG;
+  const int64_t P = (int64_t)T * k;
   if (T == 0) {
     // no rows: every weight gradient is zero, and nothing else exists
     if (E > 0 && (!dw_gate_up || !dw_down)) return MOE_ERR_ARG;
@@ -336,12 +384,9 @@ moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d
   const bf16_t* wd = (const bf16_t*)w_down;
   hipStream_t s = (hipStream_t)stream;
 
-  // the forward again, keeping what the gradients need
-  if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
-  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s)));
-  TRY(from_hip(launch_move_rows(x, T, (int64_t)d * 2, r_tok, offs, E, P, x_perm, s)));
-  TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, wgu, h, gu, s)));
-  TRY(from_hip(launch_down_bf16(h, offs, P, E, d, I, wd, y, s)));
+  // the forward again, keeping what the gradients need (or, without
+  // recompute, what moe_forward_train left in this workspace)
+  if (recompute) TRY(forward_keep(x, logits, T, d, E, k, I, w_gate_up, w_down, topk_idx, topk_w, L, ws, s));
   // combine -> routing weights (and logits) and the expert rows' gradient
   TRY(from_hip(launch_combine_bwd_bf16((const bf16_t*)dout, y, P, p_row, topk_w, topk_idx, T, k, d, E, dy, dtopk_w,
                                        dlogits, s)));
