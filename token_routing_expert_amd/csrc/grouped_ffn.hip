@@ -50,6 +50,7 @@ constexpr int kEpiPlain = 0;       // Out = A W
 constexpr int kEpiSwiglu = 1;      // Out = silu(A Wg) * (A Wu) (gate/up tiles)
 constexpr int kEpiSwigluSave = 2;  // as kEpiSwiglu, and Out2 = [A Wg | A Wu] (row stride 2N)
 constexpr int kEpiSwigluBwd = 3;   // Out = [dg | du] from dh = A W and Aux = [g | u] (row strides 2N)
+constexpr int kBwdBlocks = 1;      // column blocks whose g, u the backward epilogue loads together
 
 __device__ __forceinline__ uint2 pack4(const float* f) {
   return make_uint2((uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16),
@@ -422,15 +423,29 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
         // dg = dh u s (1 + g (1 - s)), du = dh g s, s = sigmoid(g)
         const bf16_t* grow = Aux + (t.row0 + r) * 2 * N;
         bf16_t* drow = Out + (t.row0 + r) * 2 * N;
+        // g, u of one column block first (one round trip for its eight
+        // loads), then its arithmetic
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j0 = 0; j0 < NJ; j0 += kBwdBlocks) {
+          uint2 gq[kBwdBlocks][4], uq[kBwdBlocks][4];
+#pragma unroll
+          for (int jj = 0; jj < kBwdBlocks; ++jj)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int c = t.n0 + WCOL * wn + 32 * (j0 + jj) + 8 * q4 + lc;
+              gq[jj][q4] = c < N ? *(const uint2*)(grow + c) : make_uint2(0u, 0u);
+              uq[jj][q4] = c < N ? *(const uint2*)(grow + N + c) : make_uint2(0u, 0u);
+            }
+#pragma unroll
+          for (int jj = 0; jj < kBwdBlocks; ++jj)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
+            const int j = j0 + jj;
             const int c = t.n0 + WCOL * wn + 32 * j + 8 * q4 + lc;
             if (c >= N) continue;
             float g[4], u[4], dg[4], du[4];
-            unpack4(*(const uint2*)(grow + c), g);
-            unpack4(*(const uint2*)(grow + N + c), u);
+            unpack4(gq[jj][q4], g);
+            unpack4(uq[jj][q4], u);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const float dh = acc[j][i][4 * q4 + v];
@@ -441,6 +456,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
             *(uint2*)(drow + c) = pack4(dg);
             *(uint2*)(drow + N + c) = pack4(du);
           }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
