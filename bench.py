@@ -281,6 +281,38 @@ def main() -> int:
     graph_ms = g0.elapsed_time(g1) / args.steps
     del graph
 
+    # ---- timed region 2c: the permutation with its row moves (moe_permute
+    # with x_perm), the step as the benchmark defines it: each token row read
+    # once and written to its k grouped rows, plus the index arrays.  The
+    # fused bf16 layer skips the row copy (its gate/up reads token rows in
+    # place), so this is reported beside the layer.
+    xp_rows = torch.empty((P, d), dtype=dev_dtype, device="cuda")
+    pr_tok = torch.empty(P, dtype=torch.int32, device="cuda")
+    pr_row = torch.empty(P, dtype=torch.int32, device="cuda")
+    pr_off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+
+    def run_permute_rows():
+        st = lib.moe_permute(ptr(x), dt, T, d, k, ptr(topk_idx), E, ptr(xp_rows), ptr(pr_tok), ptr(pr_row),
+                             ptr(pr_off), ptr(pws), pws_bytes, sp)
+        if st != 0:
+            raise RuntimeError(f"moe_permute failed with status {st}")
+    for _ in range(args.warmup):
+        run_permute_rows()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    p0.record(stream)
+    for _ in range(args.steps):
+        run_permute_rows()
+    p1.record(stream)
+    torch.cuda.synchronize()
+    pr_ms = p0.elapsed_time(p1) / args.steps
+    s_elem = 4 if inp.dtype == "f32" else 2
+    pr_bytes = T * d * s_elem * (1 + k) + 16 * P
+    permute_rows = {"ms": round(pr_ms, 5), "bytes_per_call": pr_bytes,
+                    "gbs": round(pr_bytes / (pr_ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(pr_bytes / (pr_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del xp_rows
+
     # ---- timed region 3 (reported beside the layer, not part of it): the
     # router projection fused with routing, x @ W_r^T then top-k, on the
     # workload's tokens and a seeded router weight [E, d] ----
@@ -429,7 +461,8 @@ def main() -> int:
         "staged_ms_per_step": staged_ms,
         "staged_gpu_ms_per_step": gpu_ms,
         "graph_ms_per_step": graph_ms,
-        "permute_gbs": kernels["permute"].get("gbs"),
+        "permute_gbs": permute_rows["gbs"],
+        "permute_rows": permute_rows,
         "router_projection": router,
         "backward": backward,
     }

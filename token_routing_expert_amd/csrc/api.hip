@@ -147,7 +147,7 @@ moe_status moe_permute(const void* x, moe_dtype dt, int32_t T, int32_t d, int32_
   hipStream_t s = (hipStream_t)stream;
   TRY(from_hip(launch_permute_index(pair_expert, P, k, E, row_token, pair_row, expert_offsets, workspace, s)));
   if (!x_perm) return MOE_OK;   // index only: the caller gathers rows itself
-  return from_hip(launch_move_rows(x, T, (int64_t)d * elem_size(dt), row_token, expert_offsets, E, P, x_perm, s));
+  return from_hip(launch_move_rows(x, T, k, (int64_t)d * elem_size(dt), pair_row, P, x_perm, s));
 }
 
 size_t moe_grouped_ffn_workspace_size(int32_t max_rows, int32_t E, int32_t d, int32_t I, moe_dtype dt) {
@@ -283,7 +283,7 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
     TRY(from_hip(launch_down_bf16((const bf16_t*)h, offs, P, E, d, I, (const bf16_t*)w_down, (bf16_t*)y_perm, s)));
     return from_hip(launch_combine_bf16((const bf16_t*)y_perm, P, p_row, topk_w, T, k, d, (bf16_t*)out, s));
   }
-  TRY(from_hip(launch_move_rows(x, T, (int64_t)d * elem_size(dt), r_tok, offs, E, P, x_perm, s)));
+  TRY(from_hip(launch_move_rows(x, T, k, (int64_t)d * elem_size(dt), p_row, P, x_perm, s)));
   TRY(from_hip(launch_grouped_ffn_f32((const float*)x_perm, offs, P, E, d, I, (const float*)w_gate_up,
                                       (const float*)w_down, (float*)h, (float*)y_perm, s)));
   return from_hip(launch_combine_f32((const float*)y_perm, P, p_row, topk_w, T, k, d, (float*)out, s));
@@ -327,7 +327,7 @@ moe_status forward_keep(const void* x, const float* logits, int32_t T, int32_t d
   bf16_t* y = (bf16_t*)(ws + L.y);
   if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
   TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s)));
-  TRY(from_hip(launch_move_rows(x, T, (int64_t)d * 2, r_tok, offs, E, P, x_perm, s)));
+  TRY(from_hip(launch_move_rows(x, T, k, (int64_t)d * 2, p_row, P, x_perm, s)));
   TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up, h, gu, s)));
   return from_hip(launch_down_bf16(h, offs, P, E, d, I, (const bf16_t*)w_down, y, s));
 }

@@ -57,7 +57,56 @@ struct Vec<float> {
   }
 };
 
-template <typename Elem>
+// Up to KS slots: each lane first loads its vector of every slot's row (a
+// row index clamped into range, a dropped slot's value discarded by a
+// select), for two vectors at a time, so 2 KS gathers are in flight together.
+template <typename Elem, int KS>
+__device__ __forceinline__ void combine_token(const u32x4* __restrict__ y, int64_t max_rows,
+                                              const int32_t* __restrict__ pair_row, const float* __restrict__ pair_w,
+                                              int64_t t, int k, int64_t vec_per_row, u32x4* __restrict__ out) {
+  constexpr int n = Vec<Elem>::n;
+  const int lane = threadIdx.x % kWave;
+  int64_t row[KS];
+  float wt[KS];
+  bool live[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const int64_t r = j < k ? pair_row[t * k + j] : -1;
+    live[j] = r >= 0 && r < max_rows;
+    row[j] = live[j] ? r : 0;
+    wt[j] = (j < k && pair_w) ? pair_w[t * k + j] : 1.f;
+  }
+  for (int64_t v0 = lane; v0 < vec_per_row; v0 += 2 * kWave) {
+    u32x4 g[2][KS];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t v = v0 + h * kWave;
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        if (j < k && max_rows > 0 && v < vec_per_row) g[h][j] = y[row[j] * vec_per_row + v];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t v = v0 + h * kWave;
+      if (v >= vec_per_row) continue;
+      float acc[n];
+#pragma unroll
+      for (int i = 0; i < n; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        if (j >= k || !live[j]) continue;
+        float f[n];
+        Vec<Elem>::load(g[h][j], f);
+#pragma unroll
+        for (int i = 0; i < n; ++i) acc[i] = fmaf(wt[j], f[i], acc[i]);
+      }
+      out[t * vec_per_row + v] = Vec<Elem>::store(acc);
+    }
+  }
+}
+
+// KS > 0: at most KS slots (combine_token); KS == 0: any k, one slot at a time
+template <typename Elem, int KS>
 __global__ __launch_bounds__(kThreads) void k_combine(const u32x4* __restrict__ y, int64_t max_rows,
                                                       const int32_t* __restrict__ pair_row,
                                                       const float* __restrict__ pair_w, int64_t n_tok, int k,
@@ -65,6 +114,10 @@ __global__ __launch_bounds__(kThreads) void k_combine(const u32x4* __restrict__ 
   constexpr int n = Vec<Elem>::n;
   const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   if (t >= n_tok) return;
+  if constexpr (KS > 0) {
+    combine_token<Elem, KS>(y, max_rows, pair_row, pair_w, t, k, vec_per_row, out);
+    return;
+  }
   const int lane = threadIdx.x % kWave;
   for (int64_t v = lane; v < vec_per_row; v += kWave) {
     float acc[n];
@@ -139,8 +192,15 @@ hipError_t launch(const Elem* y, int64_t max_rows, const int32_t* pair_row, cons
                   int k, int d, Elem* out, hipStream_t s) {
   const int64_t vec_per_row = (int64_t)d * sizeof(Elem) / 16;
   const int64_t blocks = ceil_div(n_tok, kThreads / kWave);
-  k_combine<Elem><<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)y, max_rows, pair_row, pair_w, n_tok, k,
-                                                       vec_per_row, (u32x4*)out);
+  if (k <= 4)
+    k_combine<Elem, 4><<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)y, max_rows, pair_row, pair_w, n_tok, k,
+                                                            vec_per_row, (u32x4*)out);
+  else if (k <= 8)
+    k_combine<Elem, 8><<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)y, max_rows, pair_row, pair_w, n_tok, k,
+                                                            vec_per_row, (u32x4*)out);
+  else
+    k_combine<Elem, 0><<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)y, max_rows, pair_row, pair_w, n_tok, k,
+                                                            vec_per_row, (u32x4*)out);
   return hipGetLastError();
 }
 

@@ -104,15 +104,15 @@ hipError_t launch_route_project_f32(const float* x, const float* w_router, int T
 // Stable grouping of pairs by expert: per-chunk expert counts (chunks of
 // kPermuteChunk pairs), then the scatter, which also scans the counts when
 // there are few enough of them (else a one-workgroup scan runs between).
-constexpr int kPermuteChunk = 1024;
+constexpr int kPermuteChunk = 512;
 size_t permute_index_workspace(int64_t P, int E);
 hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E,
                                 int32_t* row_token, int32_t* pair_row, int32_t* expert_offsets,
                                 void* ws, hipStream_t s);
-// x_perm[r] = x[row_token[r]] for r < expert_offsets[E]; row_bytes % 16 == 0.
-hipError_t launch_move_rows(const void* x, int64_t T, int64_t row_bytes, const int32_t* row_token,
-                            const int32_t* expert_offsets, int E, int64_t max_rows, void* x_perm,
-                            hipStream_t s);
+// x_perm[pair_row[t*k+j]] = x[t] for every pair with a row (token-major:
+// each row of x is read once); row_bytes % 16 == 0.
+hipError_t launch_move_rows(const void* x, int64_t T, int k, int64_t row_bytes, const int32_t* pair_row,
+                            int64_t max_rows, void* x_perm, hipStream_t s);
 
 // Grouped SwiGLU feed-forward, as two launches (gate/up + SwiGLU, then down).
 // h: [max_rows, I] of the activation type.

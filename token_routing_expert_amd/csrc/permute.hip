@@ -185,28 +185,38 @@ __global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __rest
   }
 }
 
-// One wave per destination row; the rows past offsets[E] are left alone.
+// One wave per token: the token's row is read once, in pieces of up to
+// kMoveVec 16-byte vectors per lane held in registers, and each piece is
+// written to every grouped row the token's pairs landed in (pair_row; -1 and
+// rows past max_rows are skipped).  Every byte of x is read once and every
+// byte of x_perm written once, all in full 16-byte vectors.
+constexpr int kMoveVec = 8;
+
 __global__ __launch_bounds__(kThreads) void k_move_rows(const u32x4* __restrict__ x, int64_t T, int64_t vec_per_row,
-                                                        const int32_t* __restrict__ row_token,
-                                                        const int32_t* __restrict__ offsets, int E,
+                                                        const int32_t* __restrict__ pair_row, int k,
                                                         int64_t max_rows, u32x4* __restrict__ x_perm) {
-  const int64_t n_rows = clampi<int64_t>(offsets[E], 0, max_rows);
-  const int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-  if (r >= n_rows) return;
-  const int64_t t = row_token[r];
-  if (t < 0 || t >= T) return;
-  const u32x4* src = x + t * vec_per_row;
-  u32x4* dst = x_perm + r * vec_per_row;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
   const int lane = threadIdx.x % kWave;
-  int64_t v = lane;
-  for (; v + 3 * kWave < vec_per_row; v += 4 * kWave) {
-    const u32x4 a = src[v], b = src[v + kWave], c = src[v + 2 * kWave], d = src[v + 3 * kWave];
-    dst[v] = a;
-    dst[v + kWave] = b;
-    dst[v + 2 * kWave] = c;
-    dst[v + 3 * kWave] = d;
+  const u32x4* src = x + t * vec_per_row;
+  for (int64_t base = 0; base < vec_per_row; base += kMoveVec * kWave) {
+    u32x4 piece[kMoveVec];
+#pragma unroll
+    for (int i = 0; i < kMoveVec; ++i) {
+      const int64_t v = base + i * kWave + lane;
+      if (v < vec_per_row) piece[i] = src[v];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = pair_row[t * k + j];
+      if (r < 0 || r >= max_rows) continue;
+      u32x4* dst = x_perm + r * vec_per_row;
+#pragma unroll
+      for (int i = 0; i < kMoveVec; ++i) {
+        const int64_t v = base + i * kWave + lane;
+        if (v < vec_per_row) dst[v] = piece[i];
+      }
+    }
   }
-  for (; v < vec_per_row; v += kWave) dst[v] = src[v];
 }
 
 }  // namespace
@@ -234,13 +244,12 @@ hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, in
   return hipGetLastError();
 }
 
-hipError_t launch_move_rows(const void* x, int64_t T, int64_t row_bytes, const int32_t* row_token,
-                            const int32_t* expert_offsets, int E, int64_t max_rows, void* x_perm,
-                            hipStream_t s) {
-  const int rows_per_block = kThreads / kWave;
-  const int64_t blocks = ceil_div(max_rows, rows_per_block);
-  k_move_rows<<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)x, T, row_bytes / 16, row_token,
-                                                    expert_offsets, E, max_rows, (u32x4*)x_perm);
+hipError_t launch_move_rows(const void* x, int64_t T, int k, int64_t row_bytes, const int32_t* pair_row,
+                            int64_t max_rows, void* x_perm, hipStream_t s) {
+  const int tokens_per_block = kThreads / kWave;
+  const int64_t blocks = ceil_div(T, tokens_per_block);
+  k_move_rows<<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)x, T, row_bytes / 16, pair_row, k, max_rows,
+                                                    (u32x4*)x_perm);
   return hipGetLastError();
 }
 
