@@ -430,7 +430,7 @@ def main() -> int:
         traffic = float(rec["hbm_bytes_per_launch"])
     roofline = {
         "bound": "mfma",
-        "kernel": "gate/up grouped GEMM + SwiGLU (dma::k_grouped_gemm<true, ...>, tile shape chosen per call)" if inp.dtype == "bf16"
+        "kernel": "gate/up grouped GEMM + SwiGLU (dma::k_grouped_gemm<1, false, ...>, tile shape chosen per call)" if inp.dtype == "bf16"
                   else "gate/up grouped FFN (k_ffn_gate_up_f32)",
         "achieved": gu.get("tflops"),
         "peak": peak_mm,
