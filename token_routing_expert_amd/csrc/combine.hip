@@ -33,7 +33,7 @@ struct Vec<bf16_t> {
     u32x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      v[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+      v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     return v;
   }
 };

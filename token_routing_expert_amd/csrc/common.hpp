@@ -27,6 +27,16 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
+// Two floats rounded to nearest even and packed, lo in bits [15:0]: one
+// v_cvt_pk_bf16_f32 (a scalar conversion per value followed by a shift and an
+// OR costs three more instructions).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 template <typename T>
 __device__ __forceinline__ T clampi(T v, T lo, T hi) {
   return v < lo ? lo : (v > hi ? hi : v);
@@ -48,6 +58,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// A wave-uniform pointer, marked as such (both halves through readfirstlane).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // LDS (address space 3) byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -61,6 +79,19 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+// The same load with a scalar byte offset added to the lane offset: a loop
+// that walks k-stages advances one scalar register instead of recomputing
+// every lane's offset.  voffset + soffset must stay inside the buffer for
+// the lanes that load (lanes parked past num_records by voffset alone still
+// read zeros).
+__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, uint32_t voffset,
+                                       uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
                : "memory");
 }
 

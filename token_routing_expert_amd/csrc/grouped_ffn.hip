@@ -14,16 +14,19 @@
 // bf16 path (MFMA, gfx950), one kernel template with two instances: gate/up
 // with the SwiGLU epilogue (output H) and down (output Y), both bf16 with
 // float32 accumulation in v_mfma_f32_32x32x16_bf16:
-//   * workgroup tile 128 rows x 256 weight columns, 4 waves in 2 x 2, each
-//     wave 64 x 128 (2 x 4 MFMA tiles); for gate/up the 256 columns are 128
-//     gate columns and the matching 128 up columns, and each wave holds gate
-//     column j and up column j in the same lane, so SwiGLU is elementwise in
-//     registers;
-//   * k-stages of 32 stream through a ring of three LDS buffers filled by
-//     buffer loads that write LDS directly; the stages of all tiles of a
-//     workgroup form one stream, so the next tile's first stages load while
-//     the current tile finishes; two workgroups per CU, so one workgroup's
-//     waits overlap the other's multiplications;
+//   * each wave computes 64 rows x 128 weight columns (2 x 4 MFMA tiles);
+//     workgroup tiles are 256 x 256 (8 waves in ping-pong, one workgroup per
+//     CU) for large experts, 128 x 256 (4 waves, two workgroups per CU)
+//     otherwise; for gate/up the 256 columns are 128 gate columns and the
+//     matching 128 up columns, and each wave holds gate column j and up
+//     column j in the same lane, so SwiGLU is elementwise in registers;
+//   * k-stages of 32 stream through a ring of LDS buffers filled by buffer
+//     loads that write LDS directly; the stages of all tiles of a workgroup
+//     form one stream, so the next tile's first stages load while the
+//     current tile finishes.  The stage loop is unrolled over the ring, so
+//     ring slots and LDS addresses are constants and a stage costs four
+//     loads, the LDS reads and the MFMAs plus a handful of scalar
+//     instructions;
 //   * the gate/up activation loads gather token rows through row_token (the
 //     index of each tile is itself fetched into LDS by DMA a tile ahead);
 //   * weight rows are n-contiguous and reach the MFMA through the gfx950
@@ -36,6 +39,8 @@
 // float32 path: plain per-element dot products (small, for the float32
 // workloads).
 #include "common.hpp"
+
+#include <type_traits>
 
 namespace tre {
 namespace {
@@ -53,8 +58,7 @@ constexpr int kEpiSwigluBwd = 3;   // Out = [dg | du] from dh = A W and Aux = [g
 constexpr int kBwdBlocks = 1;      // column blocks whose g, u the backward epilogue loads together
 
 __device__ __forceinline__ uint2 pack4(const float* f) {
-  return make_uint2((uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16),
-                    (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16));
+  return make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
 }
 
 __device__ __forceinline__ void unpack4(uint2 v, float* f) {
@@ -145,19 +149,6 @@ struct Tile {
   int n0;
 };
 
-// Wait until this wave's loads of the stage that has `after` stages issued
-// behind it are complete (loads retire in issue order; at most MAXN stages
-// are ever in flight behind it).
-template <int PER_STAGE, int MAXN>
-__device__ __forceinline__ void wait_for_stage(int64_t after) {
-  if constexpr (MAXN == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (after >= MAXN) wait_vmcnt<MAXN * PER_STAGE>();
-    else wait_for_stage<PER_STAGE, MAXN - 1>(after);
-  }
-}
-
 // The tiles of one workgroup form a single stream of k-stages: stage g of
 // the stream lives in ring buffer g % NS, and while stage g is multiplied,
 // stages g+1 .. g+NS-1 are in flight, whichever tiles they belong to -- so
@@ -245,12 +236,21 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   };
 
   // ---- issue side: the tile whose stages are being loaded ----
-  int64_t i_tile = 0;
-  int i_k = 0, i_cursor = 0;
+  // Loop counters are 32-bit: a workgroup's stage count stays far below 2^31
+  // (rows * K < 2^31 is checked on the host).
+  int i_tile = 0, i_k = 0;
+  int i_cursor = 0;
   Tile inext = decode(vb, i_cursor);  // the tile the issue side enters next
   __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferConfig);
   __amdgpu_buffer_rsrc_t b_rsrc = a_rsrc;
   uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
+  // byte offsets of the next stage's k-columns in the activation and weight
+  // buffers: scalar, added to every lane's offset by the load itself
+  uint32_t ka = 0, kb = 0;
+  constexpr uint32_t kAStep = BK * 2;
+  const uint32_t kb_step = BT ? (uint32_t)BK * 2u : (uint32_t)BK * (uint32_t)ldw * 2u;
+  const uint32_t a_lds0 = lds_address(sA) + wave * 1024;
+  const uint32_t b_lds0 = lds_address(sB) + wave * 1024;
 
   // wave 0 copies the token index of grouped rows t.row0 .. t.row0+rows-1
   // into s_rt[slot] (rows past the tile read as 0 and are never used)
@@ -266,18 +266,21 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   // row_token the whole token matrix) and this expert's weights: a load past
   // num_records returns zeros.  Activation instruction p of this wave fills
   // rows (wave + WAVES p) RPI + lane / CPR; weight instruction p fills k-rows
-  // (wave + WAVES p) BRPI + lane / BCPR.
+  // (wave + WAVES p) BRPI + lane / BCPR.  The lane offsets address k-stage 0;
+  // every lane that loads stays inside its buffer up to the last stage.
   auto enter = [&]() {
     const Tile t = inext;
-    const int slot = (int)(i_tile & 1);
-    a_rsrc = row_token ? __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(a_rows * K * 2), kBufferConfig)
-                       : __builtin_amdgcn_make_buffer_rsrc((void*)(A + t.row0 * K), (short)0, t.rows * K * 2,
-                                                           kBufferConfig);
+    const int slot = i_tile & 1;
+    // (bases and sizes pass through readfirstlane: they are wave-uniform,
+    // and saying so keeps the descriptors in scalar registers)
+    a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(row_token ? (const void*)A : (const void*)(A + t.row0 * K)), (short)0,
+        __builtin_amdgcn_readfirstlane(row_token ? (int)(a_rows * K * 2) : t.rows * K * 2), kBufferConfig);
     // one expert's weights: [K][ldw] (read transposed by the LDS reads), or
     // with BT [N][K] (rows of k, read like the activations)
     const int64_t w_elems = BT ? (int64_t)N * K : (int64_t)K * ldw;
-    b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)t.e * w_elems), (short)0, (int)(w_elems * 2),
-                                               kBufferConfig);
+    b_rsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(W + (int64_t)t.e * w_elems), (short)0,
+                                               __builtin_amdgcn_readfirstlane((int)(w_elems * 2)), kBufferConfig);
 #pragma unroll
     for (int p = 0; p < GE::A_INSTR; ++p) {
       const int r = (wave + WAVES * p) * GE::RPI + lane / GE::CPR;
@@ -313,22 +316,27 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
       }
       b_voff[p] = ok ? (uint32_t)(kr * ldw + gcol) * 2u : kOutOfRange;
     }
+    ka = 0;
+    kb = 0;
     if (i_tile + 1 < my_tiles) {
-      inext = decode(vb + (i_tile + 1) * G, i_cursor);
+      inext = decode(vb + (int64_t)(i_tile + 1) * G, i_cursor);
       if (row_token) index_dma(inext, slot ^ 1);
     }
   };
 
-  auto issue_next = [&](int buf) {
+  // load the next stage of the stream into ring slot SLOT (a constant, so
+  // every LDS address below is a fixed offset from the wave's base)
+  auto issue = [&](auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
     if (i_k == 0) enter();
-    const uint32_t ka = (uint32_t)i_k * BK * 2u;
-    const uint32_t kb = BT ? (uint32_t)i_k * BK * 2u : (uint32_t)i_k * BK * ldw * 2u;
-    const uint32_t a_lds = lds_address(sA + buf * GE::A_BYTES) + wave * 1024;
-    const uint32_t b_lds = lds_address(sB + buf * GE::B_BYTES) + wave * 1024;
 #pragma unroll
-    for (int p = 0; p < GE::A_INSTR; ++p) dma16(a_rsrc, a_lds + p * WAVES * 1024, a_voff[p] + ka);
+    for (int p = 0; p < GE::A_INSTR; ++p)
+      dma16s(a_rsrc, a_lds0 + SLOT * GE::A_BYTES + p * WAVES * 1024, a_voff[p], ka);
 #pragma unroll
-    for (int p = 0; p < GE::B_INSTR; ++p) dma16(b_rsrc, b_lds + p * WAVES * 1024, b_voff[p] + kb);
+    for (int p = 0; p < GE::B_INSTR; ++p)
+      dma16s(b_rsrc, b_lds0 + SLOT * GE::B_BYTES + p * WAVES * 1024, b_voff[p], kb);
+    ka += kAStep;
+    kb += kb_step;
     if (++i_k == nk) {
       i_k = 0;
       ++i_tile;
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
                 // (about 1 ulp in float32, far below the bf16 rounding of h)
                 hv[u] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
               }
-              packed[h2] = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
+              packed[h2] = pack_bf16x2(hv[0], hv[1]);
             }
             *(uint2*)(orow + c) = make_uint2(packed[0], packed[1]);
             if constexpr (EPI == kEpiSwigluSave) {
@@ -464,10 +472,8 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
           for (int q4 = 0; q4 < 4; ++q4) {
             const int c = t.n0 + WCOL * wn + 32 * j + 8 * q4 + lc;
             if (c >= N) continue;
-            const uint32_t p0 = (uint32_t)f32_to_bf16(acc[j][i][4 * q4]) |
-                                ((uint32_t)f32_to_bf16(acc[j][i][4 * q4 + 1]) << 16);
-            const uint32_t p1 = (uint32_t)f32_to_bf16(acc[j][i][4 * q4 + 2]) |
-                                ((uint32_t)f32_to_bf16(acc[j][i][4 * q4 + 3]) << 16);
+            const uint32_t p0 = pack_bf16x2(acc[j][i][4 * q4], acc[j][i][4 * q4 + 1]);
+            const uint32_t p1 = pack_bf16x2(acc[j][i][4 * q4 + 2], acc[j][i][4 * q4 + 3]);
             *(uint2*)(orow + c) = make_uint2(p0, p1);
           }
       }
@@ -475,9 +481,14 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   };
 
   // ---- the stage stream ----
-  // Every tile has at least NS - 1 stages (the host guarantees it), so the
-  // token index of the next tile, fetched when a tile is entered, has landed
-  // and is visible by the time the next tile is entered.
+  // Stage g of the stream lives in ring slot g % NS.  The compute side walks
+  // its tiles; within a tile the stages run through NS copies of the stage
+  // body, one per ring slot, entered at the slot of the tile's first stage
+  // (so every slot index, LDS address and load count is a constant), and the
+  // epilogue runs once per tile after its last stage.  Every tile has at
+  // least NS - 1 stages (the host guarantees it), so the token index of the
+  // next tile, fetched when a tile is entered, has landed and is visible by
+  // the time the next tile is entered.
   auto barrier = [&]() { stage_barrier(); };
   if (row_token) {
     // the first tile's index, before anything else is in flight
@@ -485,69 +496,70 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     wait_vmcnt<0>();
     barrier();
   }
-  for (int s = 0; s < NS - 1 && s < total_stages; ++s) issue_next(s);
+  const int total = (int)total_stages;
+  issue(std::integral_constant<int, 0>{});
+  if (1 < total) issue(std::integral_constant<int, 1>{});
+  if constexpr (NS > 3) {
+    if (2 < total) issue(std::integral_constant<int, 2>{});
+  }
+  if constexpr (NS > 4) {
+    if (3 < total) issue(std::integral_constant<int, 3>{});
+  }
 
-  int c_k = 0, c_cursor = 0, buf = 0;
-  int64_t c_tile = 0;
+  int g = 0;
+  int c_cursor = 0;
   Tile cur = decode(vb, c_cursor);
-  zero_acc();
   Frag f0, f1;
-  auto finish_stage = [&]() {
-    buf = (buf + 1 == NS) ? 0 : buf + 1;
-    if (++c_k == nk) {
-      epilogue(cur);
-      zero_acc();
-      c_k = 0;
-      if (++c_tile < my_tiles) cur = decode(vb + c_tile * G, c_cursor);
-    }
-  };
-  if constexpr (!PP) {
-    for (int64_t g = 0; g < total_stages; ++g) {
-      // this wave's loads of stage g are done; after the barrier every
-      // wave's are, and every wave is done reading stage g - 1, whose buffer
-      // ((g - 1) mod NS) then receives stage g + NS - 1
-      wait_for_stage<GE::PER_STAGE, NS - 2>(total_stages - 1 - g);
+  zero_acc();
+
+  // One stage of the stream in ring slot SLOT; returns false after the
+  // tile's last stage.
+  auto stage = [&](auto slot_c, bool active, int& left) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    constexpr int ISSUE = (SLOT + NS - 1) % NS;  // the slot stage g + NS - 1 lands in
+    const char* a_buf = sA + SLOT * GE::A_BYTES;
+    const char* b_buf = sB + SLOT * GE::B_BYTES;
+    const bool more = g + NS - 1 < total;
+    if constexpr (!PP) {
+      // this wave's loads of stage g are done (NS - 2 later stages may still
+      // be in flight); after the barrier every wave's are, and every wave is
+      // done reading stage g - 1, whose slot then receives stage g + NS - 1
+      if (g + NS - 2 < total) wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
+      else wait_vmcnt<0>();
       barrier();
-      if (g + NS - 1 < total_stages) issue_next(buf == 0 ? NS - 1 : buf - 1);
+      if (more) issue(std::integral_constant<int, ISSUE>{});
       // all of the stage's fragments first, then its multiplications: the
       // reads of the second k-step are in flight during the first k-step's
       // MFMAs.  A wave whose 64 rows are all past the tile's rows has nothing
       // to multiply.
-      if (64 * wm < cur.rows) {
-        read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 0, f0);
-        read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 1, f1);
+      if (active) {
+        read_frag(a_buf, b_buf, 0, f0);
+        read_frag(a_buf, b_buf, 1, f1);
         __builtin_amdgcn_sched_barrier(0);
         mma(f0);
         mma(f1);
       }
-      finish_stage();
-    }
-  } else {
-    // Ping-pong: waves 0-3 and waves 4-7 (one of each per SIMD) run the same
-    // body -- read the stage's fragments (and issue the loads of stage
-    // g + NS - 1), barrier, multiply, barrier -- with waves 4-7 one barrier
-    // behind, so that on every SIMD one wave multiplies while the other
-    // reads.  Stage g is read by waves 0-3 between barriers 2g and 2g+1 and
-    // by waves 4-7 between 2g+1 and 2g+2; its buffer is refilled (with stage
-    // g + NS) in the read phase of stage g + 1, which starts after barrier
-    // 2g + 2.  Each wave waits for its own loads of stage g + 1 before the
-    // barrier that ends its read phase of stage g, so every wave's share of
-    // stage g + 1 has landed before barrier 2g + 2.
-    const int grp = wave / 4;
-    wait_for_stage<GE::PER_STAGE, NS - 2>(total_stages - 1);
-    barrier();
-    if (grp == 1) barrier();
-    for (int64_t g = 0; g < total_stages; ++g) {
-      if (g + NS - 1 < total_stages) issue_next(buf == 0 ? NS - 1 : buf - 1);
+    } else {
+      // Ping-pong: waves 0-3 and waves 4-7 (one of each per SIMD) run the
+      // same body -- read the stage's fragments (and issue the loads of stage
+      // g + NS - 1), barrier, multiply, barrier -- with waves 4-7 one barrier
+      // behind, so that on every SIMD one wave multiplies while the other
+      // reads.  Stage g is read by waves 0-3 between barriers 2g and 2g+1 and
+      // by waves 4-7 between 2g+1 and 2g+2; its slot is refilled (with stage
+      // g + NS) in the read phase of stage g + 1, which starts after barrier
+      // 2g + 2.  Each wave waits for its own loads of stage g + 1 before the
+      // barrier that ends its read phase of stage g, so every wave's share of
+      // stage g + 1 has landed before barrier 2g + 2.
+      if (more) issue(std::integral_constant<int, ISSUE>{});
       // a wave whose 64 rows are all past the tile's rows has nothing to
       // multiply: its SIMD then serves the other group alone (tiles of an
       // expert's last rows run up to twice as fast)
-      const bool active = 64 * wm < cur.rows;
       if (active) {
-        read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 0, f0);
-        read_frag(sA + buf * GE::A_BYTES, sB + buf * GE::B_BYTES, 1, f1);
+        read_frag(a_buf, b_buf, 0, f0);
+        read_frag(a_buf, b_buf, 1, f1);
       }
-      wait_for_stage<GE::PER_STAGE, NS - 2>(total_stages - 2 - g);
+      if (more) wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
+      else wait_vmcnt<0>();
       wait_lgkm0();
       barrier();
       if (active) {
@@ -556,10 +568,45 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
         mma(f1);
         __builtin_amdgcn_s_setprio(0);
       }
-      finish_stage();
       barrier();
     }
-    if (grp == 0) barrier();
+    ++g;
+    return --left > 0;
+  };
+
+  if constexpr (PP) {
+    // waves 4-7 start one barrier behind (see the stage body)
+    wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
+    barrier();
+    if (wave >= 4) barrier();
+  }
+  for (int c_tile = 0; c_tile < my_tiles; ++c_tile) {
+    const bool active = 64 * wm < cur.rows;
+    int left = nk;
+    // the unrolled ring, entered at the slot of the tile's first stage: the
+    // copies before it are skipped in the first round only (one entry, so
+    // the loop stays reducible and its control flow uniform)
+    int first = g % NS;
+    while (true) {
+      if (first <= 0 && !stage(std::integral_constant<int, 0>{}, active, left)) break;
+      if (first <= 1 && !stage(std::integral_constant<int, 1>{}, active, left)) break;
+      if constexpr (NS > 2) {
+        if (first <= 2 && !stage(std::integral_constant<int, 2>{}, active, left)) break;
+      }
+      if constexpr (NS > 3) {
+        if (first <= 3 && !stage(std::integral_constant<int, 3>{}, active, left)) break;
+      }
+      if constexpr (NS > 4) {
+        if (first <= 4 && !stage(std::integral_constant<int, 4>{}, active, left)) break;
+      }
+      first = 0;
+    }
+    epilogue(cur);
+    zero_acc();
+    if (c_tile + 1 < my_tiles) cur = decode(vb + (int64_t)(c_tile + 1) * G, c_cursor);
+  }
+  if constexpr (PP) {
+    if (wave < 4) barrier();
   }
 }
 

@@ -158,8 +158,7 @@ __global__ __launch_bounds__(256, 2) void k_wgrad(const bf16_t* __restrict__ a, 
 #pragma unroll
         for (int v = 0; v < 4; ++v) f[v] = acc[j][i][4 * q4 + v];
         *(uint2*)(out + (int64_t)m * N + n) =
-            make_uint2((uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16),
-                       (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16));
+            make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
       }
   }
 }
