@@ -184,9 +184,12 @@ def check_permute(tre, x, pair_expert, k, E):
 
 @pytest.mark.parametrize("T,k,E,d,dtype", [
     (3001, 3, 37, 128, "bf16"),     # several chunks, ragged tail
-    (1024, 1, 256, 64, "f32"),      # exactly one chunk, widest E
+    (1024, 1, 256, 64, "f32"),      # one-workgroup grouping, widest E
     (5, 2, 1, 192, "bf16"),         # one expert
     (2500, 4, 16, 256, "bf16"),
+    (1024, 2, 256, 64, "bf16"),     # 2048 pairs: the largest one-workgroup grouping, two steps
+    (2049, 1, 256, 64, "bf16"),     # 2049 pairs: the smallest chunked grouping
+    (700, 3, 5, 64, "bf16"),        # one-workgroup grouping, ragged second step
 ])
 def test_permute_random(tre, T, k, E, d, dtype):
     rng = np.random.default_rng(T + k + E)

@@ -121,6 +121,16 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Workgroup barrier after this wave's LDS accesses have completed, without
+// waiting for its global stores (which __syncthreads() also drains): for
+// loops that share only LDS between their steps and stream results out.
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,

@@ -22,6 +22,8 @@
 //   scan     only when there are many chunks (the sums above would grow as
 //            chunks^2): one workgroup writes the offsets and every chunk's
 //            starting rows, which the scatter then reads.
+//   small    up to kSmallPairs pairs: one workgroup does all of the above in
+//            one launch.
 // The row move is a separate, bandwidth-bound kernel: one wave per
 // destination row, 16-byte vectors, rows written in order.
 #include "common.hpp"
@@ -185,6 +187,102 @@ __global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __rest
   }
 }
 
+// Small batches (P <= kSmallPairs, decode-sized): one workgroup of 1024 threads does the
+// whole grouping -- counts in LDS, the exclusive scan, then the same stable
+// scatter as k_perm_scatter, 1024 pairs per step (rank = running row of the
+// expert + matching pairs in earlier waves of the step + rank among equal
+// ids in the wave) -- in one launch instead of two.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr int kSmallSteps = 2;  // pairs per thread: up to kSmallSteps * kSmallThreads pairs
+
+__global__ __launch_bounds__(kSmallThreads) void k_perm_small(const int32_t* __restrict__ pair_expert, int P,
+                                                               int k, int E, int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ pair_row,
+                                                               int32_t* __restrict__ row_token) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int running[kMaxExperts];
+  __shared__ int wave_count[kSmallWaves][kMaxExperts];
+  __shared__ int s_wave[kSmallWaves];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  // every id is read once, up front (one round trip), and kept in registers:
+  // id j of this thread is pair j * kSmallThreads + tid
+  int ids[kSmallSteps];
+#pragma unroll
+  for (int j = 0; j < kSmallSteps; ++j) {
+    const int p = j * kSmallThreads + tid;
+    ids[j] = p < P ? pair_expert[p] : -1;
+  }
+  if (tid < E) cnt[tid] = 0;
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < kSmallSteps; ++j)
+    if (ids[j] >= 0 && ids[j] < E) atomicAdd(&cnt[ids[j]], 1);
+  lds_barrier();
+  // exclusive scan of the counts (E <= 256: the first four waves)
+  {
+    const int v = tid < E ? cnt[tid] : 0;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1 && wave < 4) s_wave[wave] = x;
+    lds_barrier();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      before += (w < wave) ? s_wave[w] : 0;
+      all += s_wave[w];
+    }
+    if (tid < E) {
+      running[tid] = before + x - v;
+      offsets[tid] = before + x - v;
+    }
+    if (tid == 0) offsets[E] = all;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+  for (int j = 0; j < kSmallSteps; ++j) {
+    const int base = j * kSmallThreads;
+    if (base >= P) break;
+    for (int i = tid; i < kSmallWaves * E; i += kSmallThreads) (&wave_count[0][0])[(i / E) * kMaxExperts + i % E] = 0;
+    lds_barrier();
+    const int p = base + tid;
+    const int e = ids[j];
+    const bool valid = e >= 0 && e < E;
+    // lanes of this wave holding the same expert: eight ballots over the id bits
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t b = __ballot(set);
+      peers &= set ? b : ~b;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) wave_count[wave][e] = __popcll(peers);
+    lds_barrier();
+    if (valid) {
+      int r = running[e] + rank;
+      for (int w = 0; w < wave; ++w) r += wave_count[w][e];
+      pair_row[p] = r;
+      if (r >= 0 && r < P) row_token[r] = p / k;
+    } else if (p < P) {
+      pair_row[p] = -1;
+    }
+    lds_barrier();
+    if (tid < E) {
+      int add = 0;
+#pragma unroll
+      for (int w = 0; w < kSmallWaves; ++w) add += wave_count[w][tid];
+      running[tid] += add;
+    }
+    // the next step's zeroing is ordered after this update by its own barrier
+    lds_barrier();
+  }
+}
+
 // One wave per token: the token's row is read once, in pieces of up to
 // kMoveVec 16-byte vectors per lane held in registers, and each piece is
 // written to every grouped row the token's pairs landed in (pair_row; -1 and
@@ -229,8 +327,15 @@ size_t permute_index_workspace(int64_t P, int E) {
   return (size_t)round_up(2 * n_chunks * E * (int64_t)sizeof(int32_t), 256);
 }
 
+// Pair counts up to this many are grouped by the one-workgroup kernel.
+constexpr int64_t kSmallPairs = kSmallSteps * kSmallThreads;
+
 hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E, int32_t* row_token,
                                 int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s) {
+  if (P <= kSmallPairs) {
+    k_perm_small<<<1, kSmallThreads, 0, s>>>(pair_expert, (int)P, k, E, expert_offsets, pair_row, row_token);
+    return hipGetLastError();
+  }
   const int n_chunks = (int)ceil_div(P, kPermuteChunk);
   int32_t* chunk_count = (int32_t*)ws;
   int32_t* chunk_base = nullptr;
