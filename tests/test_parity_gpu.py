@@ -264,6 +264,7 @@ def check_grouped_ffn(tre, inp, idx):
     (520, 128, 2, 2, 256, "bf16"),    # an expert with several row tiles
     (64, 128, 8, 2, 256, "f32"),
     (77, 64, 6, 3, 64, "f32"),
+    (40, 320, 6, 2, 2048, "bf16"),    # few rows: the down projection's k-stages split in ranges
 ])
 def test_grouped_ffn_random(tre, T, d, E, k, I, dtype):
     inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype=dtype, seed=T + d, logits="normal_bias")
@@ -433,6 +434,8 @@ def test_forward_decode(tre):
     (130, 128, 4, 4, 192, "bf16", "normal"),         # k = E
     (257, 64, 3, 2, 64, "f32", "uniform"),
     (1000, 192, 7, 3, 320, "bf16", "normal_bias"),
+    (48, 256, 8, 2, 2048, "bf16", "normal"),         # few rows: k-split down projection
+    (3, 64, 2, 1, 1024, "bf16", "normal"),           # a split over two ranges, one row per expert
 ])
 def test_forward_shapes(tre, T, d, E, k, I, dtype, logits):
     inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype=dtype, seed=T + E, logits=logits)
@@ -666,6 +669,7 @@ def test_backward_empty_batch(tre):
     (300, 256, 8, 2, 320, "normal"),
     (4096, 512, 8, 2, 576, "normal_bias"),   # 256-row tiles
     (600, 128, 16, 1, 128, None),            # given pairs, some masked
+    (48, 256, 8, 2, 2048, "normal"),         # few rows: k-split down projection in both forwards
 ])
 def test_training_step_saved_equals_recompute(tre, T, d, E, k, I, logits):
     # the training forward's output equals moe_forward's bit for bit, and the

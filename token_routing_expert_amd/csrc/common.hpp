@@ -162,15 +162,20 @@ hipError_t launch_move_rows(const void* x, int64_t T, int k, int64_t row_bytes, 
 hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s,
                                const int32_t* row_token = nullptr, int64_t x_rows = 0);
+// split_ws (optional, split_workspace(max_rows, d) bytes, float32): with few
+// rows the down projection's k-stages are split over more workgroups and
+// summed there in a fixed order (deterministic).
+size_t split_workspace(int64_t max_rows, int d);
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
-                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s);
+                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws = nullptr);
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
                               int d, int I, const float* w_gate_up, float* h, hipStream_t s);
 hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                            int I, const float* w_down, float* y_perm, hipStream_t s);
 hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets,
                                    int64_t max_rows, int E, int d, int I, const bf16_t* w_gate_up,
-                                   const bf16_t* w_down, bf16_t* h, bf16_t* y_perm, hipStream_t s);
+                                   const bf16_t* w_down, bf16_t* h, bf16_t* y_perm, hipStream_t s,
+                                   float* split_ws = nullptr);
 hipError_t launch_grouped_ffn_f32(const float* x_perm, const int32_t* expert_offsets,
                                   int64_t max_rows, int E, int d, int I, const float* w_gate_up,
                                   const float* w_down, float* h, float* y_perm, hipStream_t s);

@@ -55,6 +55,7 @@ constexpr int kEpiPlain = 0;       // Out = A W
 constexpr int kEpiSwiglu = 1;      // Out = silu(A Wg) * (A Wu) (gate/up tiles)
 constexpr int kEpiSwigluSave = 2;  // as kEpiSwiglu, and Out2 = [A Wg | A Wu] (row stride 2N)
 constexpr int kEpiSwigluBwd = 3;   // Out = [dg | du] from dh = A W and Aux = [g | u] (row strides 2N)
+constexpr int kEpiPartial = 4;     // Part[split] = A W over the split's k-stages (float32, row stride N)
 constexpr int kBwdBlocks = 1;      // column blocks whose g, u the backward epilogue loads together
 
 __device__ __forceinline__ uint2 pack4(const float* f) {
@@ -160,7 +161,8 @@ template <int EPI, bool BT, int BK, int OCC, int NJ, int WM, int NS, bool PP>
 __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K, int N, int ldw,
     const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles, const int32_t* __restrict__ row_token,
-    int64_t a_rows, bf16_t* __restrict__ Out2, const bf16_t* __restrict__ Aux) {
+    int64_t a_rows, bf16_t* __restrict__ Out2, const bf16_t* __restrict__ Aux, int n_split,
+    float* __restrict__ Part) {
   // gate/up tiles: 128 gate columns and the matching 128 up columns
   constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   static_assert(!(SWIGLU && BT), "the gate/up weight is only read as [K][2N]");
@@ -204,10 +206,19 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   const int64_t total_tiles = (int64_t)total_mt * n_tiles;
   const int G = gridDim.x;
   const int vb = (blockIdx.x % kXcd) * (G / kXcd) + blockIdx.x / kXcd;
-  if (vb >= total_tiles) return;  // the whole workgroup: no barrier follows
-  const int64_t my_tiles = (total_tiles - vb + G - 1) / G;
+  // Work units: each tile's k-stages cut into n_split ranges (1: whole
+  // tiles), unit u = tile u / n_split, range u % n_split; consecutive units
+  // (one tile's ranges) go to workgroups of one XCD.
+  const int64_t total_units = total_tiles * n_split;
+  if (vb >= total_units) return;  // the whole workgroup: no barrier follows
+  const int my_tiles = (int)((total_units - vb + G - 1) / G);  // units of this workgroup
   const int nk = K / BK;
-  const int64_t total_stages = my_tiles * nk;
+  auto k_begin = [&](int split) { return split * nk / n_split; };
+  int total_stages = 0;
+  for (int i = 0; i < my_tiles; ++i) {
+    const int split = (int)((vb + (int64_t)i * G) % n_split);
+    total_stages += k_begin(split + 1) - k_begin(split);
+  }
 
   // tile v of the list; `cursor` is the expert of an earlier tile of this
   // workgroup (tiles are visited in increasing order).  Everything is
@@ -238,9 +249,10 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   // ---- issue side: the tile whose stages are being loaded ----
   // Loop counters are 32-bit: a workgroup's stage count stays far below 2^31
   // (rows * K < 2^31 is checked on the host).
-  int i_tile = 0, i_k = 0;
+  int i_tile = 0, i_k = 0, i_len = 0;
   int i_cursor = 0;
-  Tile inext = decode(vb, i_cursor);  // the tile the issue side enters next
+  Tile inext = decode(vb / n_split, i_cursor);  // the tile the issue side enters next
+  int inext_split = vb % n_split;
   __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferConfig);
   __amdgpu_buffer_rsrc_t b_rsrc = a_rsrc;
   uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
@@ -316,10 +328,14 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
       }
       b_voff[p] = ok ? (uint32_t)(kr * ldw + gcol) * 2u : kOutOfRange;
     }
-    ka = 0;
-    kb = 0;
+    const int k0 = k_begin(inext_split);
+    ka = (uint32_t)k0 * kAStep;
+    kb = (uint32_t)k0 * kb_step;
+    i_len = k_begin(inext_split + 1) - k0;
     if (i_tile + 1 < my_tiles) {
-      inext = decode(vb + (int64_t)(i_tile + 1) * G, i_cursor);
+      const int64_t u = vb + (int64_t)(i_tile + 1) * G;
+      inext = decode(u / n_split, i_cursor);
+      inext_split = (int)(u % n_split);
       if (row_token) index_dma(inext, slot ^ 1);
     }
   };
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
       dma16s(b_rsrc, b_lds0 + SLOT * GE::B_BYTES + p * WAVES * 1024, b_voff[p], kb);
     ka += kAStep;
     kb += kb_step;
-    if (++i_k == nk) {
+    if (++i_k == i_len) {
       i_k = 0;
       ++i_tile;
     }
@@ -385,7 +401,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
 
   // acc[j][i] holds output row 64 wm + 32 i + lane % 32, columns
   // col_base(j) + 8 q4 + 4 (lane / 32) + {0..3}
-  auto epilogue = [&](const Tile& t) {
+  auto epilogue = [&](const Tile& t, int split) {
     const int lr = lane % 32, lc = 4 * (lane / 32);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -425,6 +441,18 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
               *(uint2*)(srow + c) = pack4(gq);
               *(uint2*)(srow + N + c) = pack4(uq);
             }
+          }
+      } else if constexpr (EPI == kEpiPartial) {
+        // this range's float32 partial sums of the row
+        float* prow = Part + ((int64_t)split * max_rows + t.row0 + r) * N;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int c = t.n0 + WCOL * wn + 32 * j + 8 * q4 + lc;
+            if (c >= N) continue;
+            *(f32x4*)(prow + c) = f32x4{acc[j][i][4 * q4], acc[j][i][4 * q4 + 1], acc[j][i][4 * q4 + 2],
+                                        acc[j][i][4 * q4 + 3]};
           }
       } else if constexpr (EPI == kEpiSwigluBwd) {
         // acc is dh; with the saved pre-activations g, u of the row:
@@ -508,7 +536,8 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
 
   int g = 0;
   int c_cursor = 0;
-  Tile cur = decode(vb, c_cursor);
+  Tile cur = decode(vb / n_split, c_cursor);
+  int cur_split = vb % n_split;
   Frag f0, f1;
   zero_acc();
 
@@ -582,7 +611,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   }
   for (int c_tile = 0; c_tile < my_tiles; ++c_tile) {
     const bool active = 64 * wm < cur.rows;
-    int left = nk;
+    int left = k_begin(cur_split + 1) - k_begin(cur_split);
     // the unrolled ring, entered at the slot of the tile's first stage: the
     // copies before it are skipped in the first round only (one entry, so
     // the loop stays reducible and its control flow uniform)
@@ -601,9 +630,13 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
       }
       first = 0;
     }
-    epilogue(cur);
+    epilogue(cur, cur_split);
     zero_acc();
-    if (c_tile + 1 < my_tiles) cur = decode(vb + (int64_t)(c_tile + 1) * G, c_cursor);
+    if (c_tile + 1 < my_tiles) {
+      const int64_t u = vb + (int64_t)(c_tile + 1) * G;
+      cur = decode(u / n_split, c_cursor);
+      cur_split = (int)(u % n_split);
+    }
   }
   if constexpr (PP) {
     if (wave < 4) barrier();
@@ -684,15 +717,58 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float* __restrict__ 
 template <int EPI, bool BT = false, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2, int NS = 3, bool PP = false>
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
-                      int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr) {
+                      int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr, int n_split = 1,
+                      float* part = nullptr) {
   constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   constexpr int BNO = SWIGLU ? 32 * NJ : 64 * NJ;   // output columns per tile
-  if (K / BK < NS - 1) return hipErrorInvalidValue;  // each tile spans at least NS - 1 stages
+  if (K / BK / n_split < NS - 1) return hipErrorInvalidValue;  // each range spans at least NS - 1 stages
   const int nt = (int)ceil_div(N, BNO);
   dma::k_grouped_gemm<EPI, BT, BK, OCC, NJ, WM, NS, PP>
-      <<<persistent_grid(max_rows, E, 64 * WM, nt, OCC), 128 * WM, 0, s>>>(a, offsets, max_rows, E, K, N, ldw, w, out,
-                                                                          nt, row_token, a_rows, out2, aux);
+      <<<persistent_grid(max_rows, E, 64 * WM, nt * n_split, OCC), 128 * WM, 0, s>>>(
+          a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows, out2, aux, n_split, part);
   return hipGetLastError();
+}
+
+// ---- k-split products for few rows ----
+// With few rows (decode-sized batches) the weight stream is the whole cost
+// and the tiles are too few to keep every CU loading: the down projection's
+// k-stages are then cut into n_split ranges, each writing float32 partial
+// sums of its rows, and k_split_sum adds the ranges in order (deterministic)
+// and rounds the rows to bf16.
+constexpr int64_t kSplitMaxRows = 256;
+constexpr int kSplitMax = 8;
+constexpr int kSplitMinStages = 16;
+
+// One thread per 4 columns of a row.
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, int n_split,
+                                                   const int32_t* __restrict__ offsets, int E, int64_t max_rows,
+                                                   int N, bf16_t* __restrict__ out) {
+  const int64_t r = blockIdx.y;
+  const int c = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  const int64_t n_rows = clampi<int64_t>(offsets[E], 0, max_rows);
+  if (r >= n_rows || c >= N) return;
+  f32x4 sum = *(const f32x4*)(part + r * N + c);
+  for (int sp = 1; sp < n_split; ++sp) sum += *(const f32x4*)(part + ((int64_t)sp * max_rows + r) * N + c);
+  *(uint2*)(out + r * N + c) = make_uint2(pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3]));
+}
+
+// Ranges per tile for a product with few rows (1: no split).  Tiles are
+// counted for the worst case of the offsets (every expert non-empty); the
+// split that needs the fewest rounds of CU slots per unit of work wins.
+int choose_split(int64_t max_rows, int E, int K, int N, int bm, int occ) {
+  if (max_rows > kSplitMaxRows || N % 4 != 0) return 1;
+  const int64_t tiles = (max_rows / bm + (E < max_rows ? E : max_rows)) * ceil_div(N, 256);
+  const int64_t slots = (int64_t)occ * num_cus();
+  int best = 1;
+  double best_cost = (double)ceil_div(tiles, slots);
+  for (int sp = 2; sp <= kSplitMax && (K / 32) / sp >= kSplitMinStages; ++sp) {
+    const double cost = (double)ceil_div(tiles * sp, slots) / sp;
+    if (cost < 0.95 * best_cost) {
+      best = sp;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // One grouped product in the tile shape big_tiles picks.
@@ -726,8 +802,23 @@ hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, i
                                         x_rows);
 }
 
+size_t split_workspace(int64_t max_rows, int d) {
+  return max_rows <= kSplitMaxRows ? (size_t)kSplitMax * max_rows * d * sizeof(float) : 0;
+}
+
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
-                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s) {
+                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws) {
+  if (split_ws != nullptr && !big_tiles(max_rows, E, I)) {
+    const int n_split = choose_split(max_rows, E, I, d, 128, 2);
+    if (n_split > 1) {
+      const hipError_t e = launch_dma<kEpiPartial>(h, expert_offsets, max_rows, E, I, d, d, w_down, nullptr, s,
+                                                   nullptr, 0, nullptr, nullptr, n_split, split_ws);
+      if (e != hipSuccess) return e;
+      const dim3 grid((unsigned)ceil_div(d / 4, 256), (unsigned)max_rows);
+      k_split_sum<<<grid, 256, 0, s>>>(split_ws, n_split, expert_offsets, E, max_rows, d, y_perm);
+      return hipGetLastError();
+    }
+  }
   return launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
 }
 
@@ -768,10 +859,10 @@ hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_
 
 hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets, int64_t max_rows,
                                    int E, int d, int I, const bf16_t* w_gate_up, const bf16_t* w_down,
-                                   bf16_t* h, bf16_t* y_perm, hipStream_t s) {
+                                   bf16_t* h, bf16_t* y_perm, hipStream_t s, float* split_ws) {
   const hipError_t e = launch_gate_up_bf16(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s, nullptr, 0);
   if (e != hipSuccess) return e;
-  return launch_down_bf16(h, expert_offsets, max_rows, E, d, I, w_down, y_perm, s);
+  return launch_down_bf16(h, expert_offsets, max_rows, E, d, I, w_down, y_perm, s, split_ws);
 }
 
 hipError_t launch_grouped_ffn_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
