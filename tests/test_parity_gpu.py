@@ -455,6 +455,41 @@ def test_forward_many_tiles_per_workgroup(tre, T, d, E, k, I):
     check_forward(tre, inp, row_tol=TOL["bf16"])
 
 
+@pytest.mark.parametrize("T,d,E,k,I", [
+    (4096, 256, 8, 2, 4096),   # gate/up: K = 256, about 1300 tiles of 256 rows (claimed tail), light tiles mixed in
+    (8192, 4096, 8, 2, 256),   # down: K = 256, about 1100 tiles (claimed tail)
+])
+def test_forward_claimed_tail_equals_dealt_tiles(tre, T, d, E, k, I):
+    # With four or more rounds of 256-row tiles, moe_forward hands out the
+    # last rounds by a ticket counter in its workspace; the separate
+    # projections (no workspace) deal every tile round-robin.  The two must
+    # agree bit for bit on every row (each tile computed exactly once, by
+    # one workgroup); the workspace starts as NaN bytes, so a tile left out
+    # would show.  Sampled tokens against the oracle as well.
+    torch = _torch()
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + d, logits="normal_bias")
+    say(f"forward claimed tail T={T} d={d} E={E} k={k} I={I}")
+    xd, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
+    logits = to_device(inp.logits)
+    ws = torch.full((tre.moe_forward_workspace_size(T, d, E, k, I, tre.MOE_BF16),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    for _ in range(2):   # the second call reuses the workspace, counters and all
+        out, idx, w = tre.moe_forward(xd, wgu, wd, k, logits=logits, workspace=ws)
+        sync()
+        _, row_token, pair_row, offsets = tre.moe_permute(xd, idx.reshape(-1), k, E, move_rows=False)
+        h = tre.moe_gate_up_swiglu(xd, offsets, wgu, row_token=row_token, max_rows=T * k)
+        y = tre.moe_down_proj(h, offsets, wd)
+        staged = tre.moe_combine(y, pair_row, w.reshape(-1), T, k)
+        sync()
+        assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
+    ref_idx, ref_w = oracle.route(inp.logits, k)
+    sel = sample_tokens(T, 24, 3)
+    ref = oracle.moe_tokens(inp.x, ref_idx, ref_w, inp.w_gate_up, inp.w_down, tokens=sel)
+    err = rel_l2(to_host(out)[sel], ref)
+    say(f"  rel_l2={err:.3e} over {len(sel)} tokens")
+    assert err <= TOL["bf16"]
+
+
 def test_forward_all_tokens_one_expert(tre):
     inp = workloads.make_custom(T=700, d=128, E=4, k=1, I=128, dtype="bf16", seed=9, logits="normal")
     inp.logits[:, 2] += 100.0

@@ -37,7 +37,7 @@ moe_status check_width(int32_t n) {
 
 // Byte layout of the moe_forward workspace.
 struct ForwardLayout {
-  size_t pair_row, row_token, offsets, x_perm, h, y_perm, perm_ws, split, total;
+  size_t pair_row, row_token, offsets, x_perm, h, y_perm, perm_ws, split, sched, total;
 };
 
 ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, moe_dtype dt) {
@@ -53,6 +53,7 @@ ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
   L.y_perm = o;    o += align256(P * d * s);
   L.perm_ws = o;   o += permute_index_workspace(P, (int)E);
   L.split = o;     o += dt == MOE_BF16 ? align256(split_workspace(P, d)) : 0;
+  L.sched = o;     o += dt == MOE_BF16 ? align256(kSchedWords * 4) : 0;
   L.total = o;
   return L;
 }
@@ -60,7 +61,7 @@ ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
 // Byte layout of the moe_backward workspace (bf16): the recomputed forward
 // intermediates and the row gradients, each 256-byte aligned.
 struct BackwardLayout {
-  size_t pair_row, row_token, offsets, perm_ws, x_perm, h, gu, y, dy, dgu, dxp, split, total;
+  size_t pair_row, row_token, offsets, perm_ws, x_perm, h, gu, y, dy, dgu, dxp, split, sched, total;
 };
 
 BackwardLayout backward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
@@ -79,6 +80,7 @@ BackwardLayout backward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64
   L.dgu = o;       o += align256(P * 2 * I * 2);
   L.dxp = o;       o += align256(P * d * 2);
   L.split = o;     o += align256(split_workspace(P, d));
+  L.sched = o;     o += align256(kSchedWords * 4);
   L.total = o;
   return L;
 }
@@ -155,9 +157,10 @@ moe_status moe_permute(const void* x, moe_dtype dt, int32_t T, int32_t d, int32_
 size_t moe_grouped_ffn_workspace_size(int32_t max_rows, int32_t E, int32_t d, int32_t I, moe_dtype dt) {
   (void)E;
   if (max_rows < 0 || I < 1 || !dtype_ok(dt)) return 0;
-  // h, then (bf16, few rows) the down projection's k-split partial sums
+  // h, then (bf16) the down projection's k-split partial sums (few rows) and
+  // the two products' tile counters
   return align256((size_t)max_rows * I * elem_size(dt)) +
-         (dt == MOE_BF16 && d > 0 ? align256(split_workspace(max_rows, d)) : 0);
+         (dt == MOE_BF16 && d > 0 ? align256(split_workspace(max_rows, d)) + align256(kSchedWords * 4) : 0);
 }
 
 moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, int32_t max_rows, int32_t E,
@@ -174,11 +177,14 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, in
   if (!x_perm || !expert_offsets || !w_gate_up || !w_down || !y_perm) return MOE_ERR_ARG;
   if (!workspace || workspace_bytes < moe_grouped_ffn_workspace_size(max_rows, E, d, I, dt)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if (dt == MOE_BF16)
+  if (dt == MOE_BF16) {
+    char* split = (char*)workspace + align256((size_t)max_rows * I * 2);
+    int32_t* sched = (int32_t*)(split + align256(split_workspace(max_rows, d)));
+    TRY(from_hip(launch_sched_reset(sched, s)));
     return from_hip(launch_grouped_ffn_bf16((const bf16_t*)x_perm, expert_offsets, max_rows, E, d, I,
                                             (const bf16_t*)w_gate_up, (const bf16_t*)w_down, (bf16_t*)workspace,
-                                            (bf16_t*)y_perm, s,
-                                            (float*)((char*)workspace + align256((size_t)max_rows * I * 2))));
+                                            (bf16_t*)y_perm, s, (float*)split, sched));
+  }
   return from_hip(launch_grouped_ffn_f32((const float*)x_perm, expert_offsets, max_rows, E, d, I,
                                          (const float*)w_gate_up, (const float*)w_down, (float*)workspace,
                                          (float*)y_perm, s));
@@ -278,14 +284,15 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
   hipStream_t s = (hipStream_t)stream;
 
   if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
-  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s)));
+  int32_t* sched = dt == MOE_BF16 ? (int32_t*)(ws + L.sched) : nullptr;
+  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched)));
   if (dt == MOE_BF16) {
     // the gate/up projection reads the token rows in place through row_token
     // (no expert-ordered copy of x is materialised)
     TRY(from_hip(launch_gate_up_bf16((const bf16_t*)x, offs, P, E, d, I, (const bf16_t*)w_gate_up, (bf16_t*)h, s,
-                                     r_tok, T)));
+                                     r_tok, T, sched)));
     TRY(from_hip(launch_down_bf16((const bf16_t*)h, offs, P, E, d, I, (const bf16_t*)w_down, (bf16_t*)y_perm, s,
-                                  (float*)(ws + L.split))));
+                                  (float*)(ws + L.split), sched)));
     return from_hip(launch_combine_bf16((const bf16_t*)y_perm, P, p_row, topk_w, T, k, d, (bf16_t*)out, s));
   }
   TRY(from_hip(launch_move_rows(x, T, k, (int64_t)d * elem_size(dt), p_row, P, x_perm, s)));
@@ -331,10 +338,13 @@ moe_status forward_keep(const void* x, const float* logits, int32_t T, int32_t d
   bf16_t* gu = (bf16_t*)(ws + L.gu);
   bf16_t* y = (bf16_t*)(ws + L.y);
   if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
-  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s)));
+  int32_t* sched = (int32_t*)(ws + L.sched);
+  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched)));
   TRY(from_hip(launch_move_rows(x, T, k, (int64_t)d * 2, p_row, P, x_perm, s)));
-  TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up, h, gu, s)));
-  return from_hip(launch_down_bf16(h, offs, P, E, d, I, (const bf16_t*)w_down, y, s, (float*)(ws + L.split)));
+  TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up, h, gu, s, nullptr, 0,
+                                        sched)));
+  return from_hip(
+      launch_down_bf16(h, offs, P, E, d, I, (const bf16_t*)w_down, y, s, (float*)(ws + L.split), sched));
 }
 
 }  // namespace

@@ -147,13 +147,24 @@ hipError_t launch_route_project_f32(const float* x, const float* w_router, int T
 // there are few enough of them (else a one-workgroup scan runs between).
 constexpr int kPermuteChunk = 512;
 size_t permute_index_workspace(int64_t P, int E);
+// sched (optional): kSchedWords words that the grouping also sets to zero,
+// the tile counters of the grouped products that follow it
 hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E,
                                 int32_t* row_token, int32_t* pair_row, int32_t* expert_offsets,
-                                void* ws, hipStream_t s);
+                                void* ws, hipStream_t s, int32_t* sched = nullptr);
 // x_perm[pair_row[t*k+j]] = x[t] for every pair with a row (token-major:
 // each row of x is read once); row_bytes % 16 == 0.
 hipError_t launch_move_rows(const void* x, int64_t T, int k, int64_t row_bytes, const int32_t* pair_row,
                             int64_t max_rows, void* x_perm, hipStream_t s);
+
+// Tile counters of the grouped products (zero before each product that uses
+// one): the gate/up product's at sched[0], the down product's at
+// sched[kSchedDown] (64 bytes apart).  With a counter, the ping-pong kernel
+// hands out its last round and a half of tiles in order to whichever
+// workgroup is free; without, every tile is dealt round-robin.
+constexpr int kSchedDown = 16;
+constexpr int kSchedWords = 32;
+hipError_t launch_sched_reset(int32_t* sched, hipStream_t s);
 
 // Grouped SwiGLU feed-forward, as two launches (gate/up + SwiGLU, then down).
 // h: [max_rows, I] of the activation type.
@@ -161,13 +172,14 @@ hipError_t launch_move_rows(const void* x, int64_t T, int k, int64_t row_bytes, 
 // the permutation's row move happens inside the load.  Without, x is x_perm.
 hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s,
-                               const int32_t* row_token = nullptr, int64_t x_rows = 0);
+                               const int32_t* row_token = nullptr, int64_t x_rows = 0, int32_t* sched = nullptr);
 // split_ws (optional, split_workspace(max_rows, d) bytes, float32): with few
 // rows the down projection's k-stages are split over more workgroups and
 // summed there in a fixed order (deterministic).
 size_t split_workspace(int64_t max_rows, int d);
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
-                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws = nullptr);
+                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws = nullptr,
+                            int32_t* sched = nullptr);
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
                               int d, int I, const float* w_gate_up, float* h, hipStream_t s);
 hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
@@ -175,7 +187,7 @@ hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_
 hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets,
                                    int64_t max_rows, int E, int d, int I, const bf16_t* w_gate_up,
                                    const bf16_t* w_down, bf16_t* h, bf16_t* y_perm, hipStream_t s,
-                                   float* split_ws = nullptr);
+                                   float* split_ws = nullptr, int32_t* sched = nullptr);
 hipError_t launch_grouped_ffn_f32(const float* x_perm, const int32_t* expert_offsets,
                                   int64_t max_rows, int E, int d, int I, const float* w_gate_up,
                                   const float* w_down, float* h, float* y_perm, hipStream_t s);
@@ -192,7 +204,8 @@ hipError_t launch_combine_f32(const float* y_perm, int64_t max_rows, const int32
 // forward gate/up that also keeps the pre-activations: gu [max_rows, 2I] = [x Wg | x Wu]
 hipError_t launch_gate_up_save_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                     int I, const bf16_t* w_gate_up, bf16_t* h, bf16_t* gu, hipStream_t s,
-                                    const int32_t* row_token = nullptr, int64_t x_rows = 0);
+                                    const int32_t* row_token = nullptr, int64_t x_rows = 0,
+                                    int32_t* sched = nullptr);
 // dy[pair_row[p]] = w_p dout[t]; dw[p] = <dout[t], y_perm[pair_row[p]]>; dlogits (when non-null) through
 // the renormalised softmax of the selected logits
 hipError_t launch_combine_bwd_bf16(const bf16_t* dout, const bf16_t* y_perm, int64_t max_rows,

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K, int N, int ldw,
     const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles, const int32_t* __restrict__ row_token,
     int64_t a_rows, bf16_t* __restrict__ Out2, const bf16_t* __restrict__ Aux, int n_split,
-    float* __restrict__ Part) {
+    float* __restrict__ Part, int32_t* __restrict__ sched) {
   // gate/up tiles: 128 gate columns and the matching 128 up columns
   constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   static_assert(!(SWIGLU && BT), "the gate/up weight is only read as [K][2N]");
@@ -182,6 +182,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   __shared__ int s_lo[kMaxExperts];
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_wave[WAVES];
+  __shared__ int s_ticket[4];  // claimed tail tickets of tiles n = 0, 1, ... in slot n % 4
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -214,11 +215,38 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   const int my_tiles = (int)((total_units - vb + G - 1) / G);  // units of this workgroup
   const int nk = K / BK;
   auto k_begin = [&](int split) { return split * nk / n_split; };
+  // Claimed tail (ping-pong tiles, whole tiles, sched != nullptr, at least
+  // four rounds of tiles): the first rs = rounds - 1 tiles of every
+  // workgroup are dealt round-robin as above; the rest, units rs G ..
+  // total_units - 1, are handed out in order by an atomic ticket counter
+  // (*sched, zero at launch), so that workgroups that drew light tiles (an
+  // expert's last rows) take more of the tail.  Each tile is still computed
+  // by exactly one workgroup, so results do not depend on who takes which.
+  // (With fewer rounds the tail is a large share of the tiles, and what its
+  // balance gains is lost to weight slices no longer shared in one XCD's L2.)
+  const bool dyn = PP && sched != nullptr && n_split == 1 && total_units >= 4 * (int64_t)G && nk >= 2 * NS;
+  const int rs = dyn ? (int)(total_units / G) - 1 : 0;
+  const int64_t tail0 = (int64_t)rs * G;
+  const int64_t n_tail = total_units - tail0;
   int total_stages = 0;
-  for (int i = 0; i < my_tiles; ++i) {
-    const int split = (int)((vb + (int64_t)i * G) % n_split);
-    total_stages += k_begin(split + 1) - k_begin(split);
+  if (!dyn) {
+    for (int i = 0; i < my_tiles; ++i) {
+      const int split = (int)((vb + (int64_t)i * G) % n_split);
+      total_stages += k_begin(split + 1) - k_begin(split);
+    }
+  } else {
+    // tile 0 (dealt); later tiles count in as they become known.  rs >= 3, so
+    // the first claim (of tile rs, when tile rs - 2 is entered) is made by
+    // the stage loop.
+    total_stages = nk;
   }
+  // unit of this workgroup's tile n, -1 past its last one
+  auto unit_of = [&](int n) -> int64_t {
+    if (!dyn) return n < my_tiles ? vb + (int64_t)n * G : -1;
+    if (n < rs) return vb + (int64_t)n * G;
+    const int t = __builtin_amdgcn_readfirstlane(s_ticket[n & 3]);
+    return (t >= 0 && t < n_tail) ? tail0 + t : -1;
+  };
 
   // tile v of the list; `cursor` is the expert of an earlier tile of this
   // workgroup (tiles are visited in increasing order).  Everything is
@@ -253,6 +281,43 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   int i_cursor = 0;
   Tile inext = decode(vb / n_split, i_cursor);  // the tile the issue side enters next
   int inext_split = vb % n_split;
+  int total = total_stages;  // stages of the tiles known so far
+  // Claiming a ticket (wave 0, one lane): the atomic's return lands in
+  // `ticket` asynchronously and is counted by vmcnt in issue order with the
+  // stage loads; it is read (written to s_ticket) only by the stage body
+  // NS - 2 stages later, after a vmcnt wait that leaves fewer loads
+  // outstanding than were issued after it.  Both steps are inline assembly so
+  // that nothing reads the register in between.
+  int ticket;  // written only by the claim, read only by the post that follows it
+  int post_cnt = 0, post_slot = 0;
+  auto claim = [&](int n) {
+    if (wave == 0) {
+      uint64_t save;
+      asm volatile(
+          "s_mov_b64 %1, exec\n\t"
+          "s_mov_b64 exec, 1\n\t"
+          "global_atomic_add %0, %2, %3, off sc0\n\t"
+          "s_mov_b64 exec, %1"
+          : "=&v"(ticket), "=&s"(save)
+          : "v"(sched), "v"(1)
+          : "memory");
+    }
+    post_cnt = NS - 1;
+    post_slot = n & 3;
+  };
+  auto post = [&]() {
+    if (wave == 0) {
+      uint64_t save;
+      asm volatile(
+          "s_mov_b64 %0, exec\n\t"
+          "s_mov_b64 exec, 1\n\t"
+          "ds_write_b32 %1, %2\n\t"
+          "s_mov_b64 exec, %0"
+          : "=&s"(save)
+          : "v"(lds_address(&s_ticket[post_slot])), "v"(ticket)
+          : "memory");
+    }
+  };
   __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferConfig);
   __amdgpu_buffer_rsrc_t b_rsrc = a_rsrc;
   uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
@@ -332,11 +397,15 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     ka = (uint32_t)k0 * kAStep;
     kb = (uint32_t)k0 * kb_step;
     i_len = k_begin(inext_split + 1) - k0;
-    if (i_tile + 1 < my_tiles) {
-      const int64_t u = vb + (int64_t)(i_tile + 1) * G;
+    const int64_t u = unit_of(i_tile + 1);
+    if (u >= 0) {
       inext = decode(u / n_split, i_cursor);
       inext_split = (int)(u % n_split);
       if (row_token) index_dma(inext, slot ^ 1);
+      if (dyn) {
+        total += nk;
+        if (i_tile + 2 >= rs) claim(i_tile + 2);
+      }
     }
   };
 
@@ -524,7 +593,6 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     wait_vmcnt<0>();
     barrier();
   }
-  const int total = (int)total_stages;
   issue(std::integral_constant<int, 0>{});
   if (1 < total) issue(std::integral_constant<int, 1>{});
   if constexpr (NS > 3) {
@@ -589,6 +657,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
       }
       if (more) wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
       else wait_vmcnt<0>();
+      if (post_cnt > 0 && --post_cnt == 0) post();
       wait_lgkm0();
       barrier();
       if (active) {
@@ -609,7 +678,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     barrier();
     if (wave >= 4) barrier();
   }
-  for (int c_tile = 0; c_tile < my_tiles; ++c_tile) {
+  for (int c_tile = 0;; ++c_tile) {
     const bool active = 64 * wm < cur.rows;
     int left = k_begin(cur_split + 1) - k_begin(cur_split);
     // the unrolled ring, entered at the slot of the tile's first stage: the
@@ -632,11 +701,10 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     }
     epilogue(cur, cur_split);
     zero_acc();
-    if (c_tile + 1 < my_tiles) {
-      const int64_t u = vb + (int64_t)(c_tile + 1) * G;
-      cur = decode(u / n_split, c_cursor);
-      cur_split = (int)(u % n_split);
-    }
+    const int64_t u = unit_of(c_tile + 1);
+    if (u < 0) break;
+    cur = decode(u / n_split, c_cursor);
+    cur_split = (int)(u % n_split);
   }
   if constexpr (PP) {
     if (wave < 4) barrier();
@@ -718,14 +786,14 @@ template <int EPI, bool BT = false, int BK = 32, int OCC = 2, int NJ = 4, int WM
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
                       int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr, int n_split = 1,
-                      float* part = nullptr) {
+                      float* part = nullptr, int32_t* sched = nullptr) {
   constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   constexpr int BNO = SWIGLU ? 32 * NJ : 64 * NJ;   // output columns per tile
   if (K / BK / n_split < NS - 1) return hipErrorInvalidValue;  // each range spans at least NS - 1 stages
   const int nt = (int)ceil_div(N, BNO);
   dma::k_grouped_gemm<EPI, BT, BK, OCC, NJ, WM, NS, PP>
       <<<persistent_grid(max_rows, E, 64 * WM, nt * n_split, OCC), 128 * WM, 0, s>>>(
-          a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows, out2, aux, n_split, part);
+          a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows, out2, aux, n_split, part, sched);
   return hipGetLastError();
 }
 
@@ -775,7 +843,8 @@ int choose_split(int64_t max_rows, int E, int K, int N, int bm, int occ) {
 template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
-                       int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr);
+                       int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr,
+                       int32_t* sched = nullptr);
 
 // 256-row tiles (8 waves in ping-pong, one workgroup per CU: each weight
 // stage feeds twice the rows) once the experts hold 128 rows or more on
@@ -786,20 +855,29 @@ bool big_tiles(int64_t max_rows, int E, int K) { return max_rows >= 128 * (int64
 template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token, int64_t a_rows,
-                       bf16_t* out2, const bf16_t* aux) {
+                       bf16_t* out2, const bf16_t* aux, int32_t* sched) {
   if (big_tiles(max_rows, E, K))
     return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
-                                                     a_rows, out2, aux);
+                                                     a_rows, out2, aux, 1, nullptr, sched);
   return launch_dma<EPI, BT>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token, a_rows, out2, aux);
 }
 
 }  // namespace
 
+__global__ __launch_bounds__(64) void k_sched_reset(int32_t* __restrict__ sched) {
+  if (threadIdx.x < kSchedWords) sched[threadIdx.x] = 0;
+}
+
+hipError_t launch_sched_reset(int32_t* sched, hipStream_t s) {
+  k_sched_reset<<<1, 64, 0, s>>>(sched);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s, const int32_t* row_token,
-                               int64_t x_rows) {
+                               int64_t x_rows, int32_t* sched) {
   return launch_auto<kEpiSwiglu, false>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token,
-                                        x_rows);
+                                        x_rows, nullptr, nullptr, sched);
 }
 
 size_t split_workspace(int64_t max_rows, int d) {
@@ -807,7 +885,8 @@ size_t split_workspace(int64_t max_rows, int d) {
 }
 
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
-                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws) {
+                            int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws,
+                            int32_t* sched) {
   if (split_ws != nullptr && !big_tiles(max_rows, E, I)) {
     const int n_split = choose_split(max_rows, E, I, d, 128, 2);
     if (n_split > 1) {
@@ -819,14 +898,15 @@ hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int6
       return hipGetLastError();
     }
   }
-  return launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s);
+  return launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s, nullptr, 0,
+                                       nullptr, nullptr, sched ? sched + kSchedDown : nullptr);
 }
 
 hipError_t launch_gate_up_save_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                     int I, const bf16_t* w_gate_up, bf16_t* h, bf16_t* gu, hipStream_t s,
-                                    const int32_t* row_token, int64_t x_rows) {
+                                    const int32_t* row_token, int64_t x_rows, int32_t* sched) {
   return launch_auto<kEpiSwigluSave, false>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token,
-                                            x_rows, gu);
+                                            x_rows, gu, nullptr, sched);
 }
 
 hipError_t launch_down_dgrad_swiglu_bf16(const bf16_t* dy, const int32_t* expert_offsets, int64_t max_rows, int E,
@@ -859,10 +939,11 @@ hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_
 
 hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets, int64_t max_rows,
                                    int E, int d, int I, const bf16_t* w_gate_up, const bf16_t* w_down,
-                                   bf16_t* h, bf16_t* y_perm, hipStream_t s, float* split_ws) {
-  const hipError_t e = launch_gate_up_bf16(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s, nullptr, 0);
+                                   bf16_t* h, bf16_t* y_perm, hipStream_t s, float* split_ws, int32_t* sched) {
+  const hipError_t e =
+      launch_gate_up_bf16(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s, nullptr, 0, sched);
   if (e != hipSuccess) return e;
-  return launch_down_bf16(h, expert_offsets, max_rows, E, d, I, w_down, y_perm, s, split_ws);
+  return launch_down_bf16(h, expert_offsets, max_rows, E, d, I, w_down, y_perm, s, split_ws, sched);
 }
 
 hipError_t launch_grouped_ffn_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,

@@ -34,9 +34,11 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void k_perm_hist(const int32_t* __restrict__ pair_expert, int64_t P,
-                                                        int E, int32_t* __restrict__ chunk_count) {
+                                                        int E, int32_t* __restrict__ chunk_count,
+                                                        int32_t* __restrict__ sched) {
   __shared__ int cnt[kMaxExperts];
   const int tid = threadIdx.x;
+  if (sched && blockIdx.x == 0 && tid < kSchedWords) sched[tid] = 0;
   if (tid < E) cnt[tid] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * kPermuteChunk;
@@ -199,12 +201,14 @@ constexpr int kSmallSteps = 2;  // pairs per thread: up to kSmallSteps * kSmallT
 __global__ __launch_bounds__(kSmallThreads) void k_perm_small(const int32_t* __restrict__ pair_expert, int P,
                                                                int k, int E, int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ pair_row,
-                                                               int32_t* __restrict__ row_token) {
+                                                               int32_t* __restrict__ row_token,
+                                                               int32_t* __restrict__ sched) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int running[kMaxExperts];
   __shared__ int wave_count[kSmallWaves][kMaxExperts];
   __shared__ int s_wave[kSmallWaves];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  if (sched && tid < kSchedWords) sched[tid] = 0;
   // every id is read once, up front (one round trip), and kept in registers:
   // id j of this thread is pair j * kSmallThreads + tid
   int ids[kSmallSteps];
@@ -331,15 +335,15 @@ size_t permute_index_workspace(int64_t P, int E) {
 constexpr int64_t kSmallPairs = kSmallSteps * kSmallThreads;
 
 hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E, int32_t* row_token,
-                                int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s) {
+                                int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s, int32_t* sched) {
   if (P <= kSmallPairs) {
-    k_perm_small<<<1, kSmallThreads, 0, s>>>(pair_expert, (int)P, k, E, expert_offsets, pair_row, row_token);
+    k_perm_small<<<1, kSmallThreads, 0, s>>>(pair_expert, (int)P, k, E, expert_offsets, pair_row, row_token, sched);
     return hipGetLastError();
   }
   const int n_chunks = (int)ceil_div(P, kPermuteChunk);
   int32_t* chunk_count = (int32_t*)ws;
   int32_t* chunk_base = nullptr;
-  k_perm_hist<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, E, chunk_count);
+  k_perm_hist<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, E, chunk_count, sched);
   if ((int64_t)n_chunks * E > kFusedScanMax) {
     chunk_base = chunk_count + (int64_t)n_chunks * E;
     k_perm_scan<<<1, kThreads, 0, s>>>(chunk_count, n_chunks, E, chunk_base, expert_offsets);
