@@ -436,6 +436,7 @@ def test_forward_decode(tre):
     (1000, 192, 7, 3, 320, "bf16", "normal_bias"),
     (48, 256, 8, 2, 2048, "bf16", "normal"),         # few rows: k-split down projection
     (3, 64, 2, 1, 1024, "bf16", "normal"),           # a split over two ranges, one row per expert
+    (200, 128, 128, 2, 256, "bf16", "normal"),       # 64-row tiles at their widest E (one thread per expert)
 ])
 def test_forward_shapes(tre, T, d, E, k, I, dtype, logits):
     inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype=dtype, seed=T + E, logits=logits)

@@ -16,8 +16,9 @@
 // float32 accumulation in v_mfma_f32_32x32x16_bf16:
 //   * each wave computes 64 rows x 128 weight columns (2 x 4 MFMA tiles);
 //     workgroup tiles are 256 x 256 (8 waves in ping-pong, one workgroup per
-//     CU) for large experts, 128 x 256 (4 waves, two workgroups per CU)
-//     otherwise; for gate/up the 256 columns are 128 gate columns and the
+//     CU) for large experts, 64 x 256 (2 waves, two workgroups per CU) for
+//     decode-sized batches and 128 x 256 (4 waves, two workgroups per CU)
+//     in between; for gate/up the 256 columns are 128 gate columns and the
 //     matching 128 up columns, and each wave holds gate column j and up
 //     column j in the same lane, so SwiGLU is elementwise in registers;
 //   * k-stages of 32 stream through a ring of LDS buffers filled by buffer
@@ -45,7 +46,6 @@
 namespace tre {
 namespace {
 
-constexpr int NTHR = 256;        // 4 waves per workgroup
 constexpr int kXcd = 8;          // XCDs per MI355X; workgroups are dealt round-robin over them
 // byte offset that is always past num_records (a buffer load there returns zeros)
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -852,6 +852,12 @@ hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows
 // per CU) below that.
 bool big_tiles(int64_t max_rows, int E, int K) { return max_rows >= 128 * (int64_t)E && K >= 96; }
 
+// 64-row tiles (two waves, two workgroups per CU) when the experts hold at
+// most 64 rows on average (decode-sized batches): the product is a weight
+// stream, and a 128-row tile would stage and multiply mostly empty rows.
+// The tile list is set up with one thread per expert, so E <= 128.
+bool small_tiles(int64_t max_rows, int E) { return max_rows <= 64 * (int64_t)E && E <= 128; }
+
 template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token, int64_t a_rows,
@@ -859,6 +865,9 @@ hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows
   if (big_tiles(max_rows, E, K))
     return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
                                                      a_rows, out2, aux, 1, nullptr, sched);
+  if (small_tiles(max_rows, E))
+    return launch_dma<EPI, BT, 32, 2, 4, 1, 3, false>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
+                                                      a_rows, out2, aux);
   return launch_dma<EPI, BT>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token, a_rows, out2, aux);
 }
 
@@ -888,10 +897,15 @@ hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int6
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws,
                             int32_t* sched) {
   if (split_ws != nullptr && !big_tiles(max_rows, E, I)) {
-    const int n_split = choose_split(max_rows, E, I, d, 128, 2);
+    const bool small = small_tiles(max_rows, E);
+    const int n_split = choose_split(max_rows, E, I, d, small ? 64 : 128, 2);
     if (n_split > 1) {
-      const hipError_t e = launch_dma<kEpiPartial>(h, expert_offsets, max_rows, E, I, d, d, w_down, nullptr, s,
-                                                   nullptr, 0, nullptr, nullptr, n_split, split_ws);
+      const hipError_t e =
+          small ? launch_dma<kEpiPartial, false, 32, 2, 4, 1, 3, false>(h, expert_offsets, max_rows, E, I, d, d,
+                                                                        w_down, nullptr, s, nullptr, 0, nullptr,
+                                                                        nullptr, n_split, split_ws)
+                : launch_dma<kEpiPartial>(h, expert_offsets, max_rows, E, I, d, d, w_down, nullptr, s, nullptr, 0,
+                                          nullptr, nullptr, n_split, split_ws);
       if (e != hipSuccess) return e;
       const dim3 grid((unsigned)ceil_div(d / 4, 256), (unsigned)max_rows);
       k_split_sum<<<grid, 256, 0, s>>>(split_ws, n_split, expert_offsets, E, max_rows, d, y_perm);
