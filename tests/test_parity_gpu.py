@@ -491,6 +491,49 @@ def test_forward_claimed_tail_equals_dealt_tiles(tre, T, d, E, k, I):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T,d,E,k,I", [
+    (2048, 256, 8, 1, 512),    # 256-row tiles: the down projection writes the output rows
+    (64, 512, 16, 1, 1024),    # few rows: the k-split sum writes the output rows
+    (300, 256, 8, 1, 256),     # neither: grouped rows, then the combine
+    (2048, 256, 8, 2, 512),    # k = 2: always the combine
+])
+def test_forward_one_pair_per_token_equals_staged(tre, T, d, E, k, I):
+    # Given pairs with every seventh one dropped (id -1).  The fused layer
+    # (output and workspace starting as NaN bytes, so a row nobody writes
+    # would show) equals the entry points run one after the other -- grouping
+    # with the row moves, the grouped feed-forward (which takes the same
+    # k-split for few rows), combine -- bit for bit, and the tokens without a
+    # pair get zero rows.
+    torch = _torch()
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + I + k,
+                                logits=None if k == 1 else "normal")
+    if k == 1:
+        pe, pw = inp.pair_expert.reshape(T, k).copy(), inp.pair_w.reshape(T, k).astype(np.float32)
+    else:
+        pe, pw = oracle.route(inp.logits, k)
+        pe, pw = pe.astype(np.int32), pw.astype(np.float32)
+    pe.reshape(-1)[::7] = -1
+    if k > 1:
+        pe[5, :] = -1   # a token with no pair at all
+    say(f"forward vs staged T={T} d={d} E={E} k={k} I={I}")
+    xd, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
+    idx, w = to_device(pe), to_device(pw)
+    ws = torch.full((tre.moe_forward_workspace_size(T, d, E, k, I, tre.MOE_BF16),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tre.moe_forward(xd, wgu, wd, k, topk_idx=idx, topk_w=w, out=out, workspace=ws)
+    x_perm, _, pair_row, offsets = tre.moe_permute(xd, idx.reshape(-1), k, E)
+    y = tre.moe_grouped_ffn(x_perm, offsets, wgu, wd)
+    staged = tre.moe_combine(y, pair_row, w.reshape(-1), T, k)
+    sync()
+    assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
+    none = np.all(pe < 0, axis=1)
+    assert none.any() and not np.any(as_f64(to_host(out)[none]))
+    ref = oracle.moe_tokens(inp.x, pe, pw.astype(np.float64), inp.w_gate_up, inp.w_down,
+                            tokens=np.arange(min(T, 64)))
+    assert rel_l2(to_host(out)[: min(T, 64)], ref) <= TOL["bf16"]
+
+
 def test_forward_all_tokens_one_expert(tre):
     inp = workloads.make_custom(T=700, d=128, E=4, k=1, I=128, dtype="bf16", seed=9, logits="normal")
     inp.logits[:, 2] += 100.0

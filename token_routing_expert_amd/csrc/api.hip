@@ -37,7 +37,7 @@ moe_status check_width(int32_t n) {
 
 // Byte layout of the moe_forward workspace.
 struct ForwardLayout {
-  size_t pair_row, row_token, offsets, x_perm, h, y_perm, perm_ws, split, sched, total;
+  size_t pair_row, row_token, offsets, x_perm, h, y_perm, perm_ws, split, sched, row_w, total;
 };
 
 ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, moe_dtype dt) {
@@ -54,6 +54,7 @@ ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
   L.perm_ws = o;   o += permute_index_workspace(P, (int)E);
   L.split = o;     o += dt == MOE_BF16 ? align256(split_workspace(P, d)) : 0;
   L.sched = o;     o += dt == MOE_BF16 ? align256(kSchedWords * 4) : 0;
+  L.row_w = o;     o += dt == MOE_BF16 && k == 1 ? align256(P * 4) : 0;
   L.total = o;
   return L;
 }
@@ -285,12 +286,24 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
 
   if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
   int32_t* sched = dt == MOE_BF16 ? (int32_t*)(ws + L.sched) : nullptr;
-  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched)));
+  // one pair per token: the down projection writes the output rows itself
+  // (times the routing weight) where its tile shape allows, and no combine
+  // pass runs
+  const bool scatter = dt == MOE_BF16 && k == 1 && down_scatters(P, E, d, I, true);
+  float* row_w = scatter ? (float*)(ws + L.row_w) : nullptr;
+  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched,
+                                    scatter ? topk_w : nullptr, row_w)));
   if (dt == MOE_BF16) {
+    if (scatter) TRY(from_hip(launch_zero_unrouted_bf16(p_row, P, T, d, (bf16_t*)out, s)));
     // the gate/up projection reads the token rows in place through row_token
     // (no expert-ordered copy of x is materialised)
     TRY(from_hip(launch_gate_up_bf16((const bf16_t*)x, offs, P, E, d, I, (const bf16_t*)w_gate_up, (bf16_t*)h, s,
                                      r_tok, T, sched)));
+    if (scatter) {
+      const DownScatter sc{(bf16_t*)out, r_tok, row_w, T};
+      return from_hip(launch_down_bf16((const bf16_t*)h, offs, P, E, d, I, (const bf16_t*)w_down, nullptr, s,
+                                       (float*)(ws + L.split), sched, &sc));
+    }
     TRY(from_hip(launch_down_bf16((const bf16_t*)h, offs, P, E, d, I, (const bf16_t*)w_down, (bf16_t*)y_perm, s,
                                   (float*)(ws + L.split), sched)));
     return from_hip(launch_combine_bf16((const bf16_t*)y_perm, P, p_row, topk_w, T, k, d, (bf16_t*)out, s));

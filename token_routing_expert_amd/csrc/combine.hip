@@ -187,6 +187,29 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(
   }
 }
 
+// One pair per token, with the down projection writing the output rows
+// itself: the rows of tokens whose pair has no grouped row (a dropped id)
+// are zero, as the combine would leave them.  One thread checks each token;
+// the wave then clears its flagged rows one after another, 16 bytes a lane.
+__global__ __launch_bounds__(kThreads) void k_zero_unrouted(const int32_t* __restrict__ pair_row, int64_t max_rows,
+                                                            int64_t T, int64_t vec_per_row,
+                                                            u32x4* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  bool dropped = false;
+  if (t < T) {
+    const int64_t r = pair_row[t];
+    dropped = r < 0 || r >= max_rows;
+  }
+  uint64_t todo = __ballot(dropped);
+  const int64_t t0 = t - lane;
+  while (todo) {
+    const int l = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    for (int64_t v = lane; v < vec_per_row; v += kWave) out[(t0 + l) * vec_per_row + v] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 template <typename Elem>
 hipError_t launch(const Elem* y, int64_t max_rows, const int32_t* pair_row, const float* pair_w, int64_t n_tok,
                   int k, int d, Elem* out, hipStream_t s) {
@@ -219,6 +242,13 @@ hipError_t launch_combine_bwd_bf16(const bf16_t* dout, const bf16_t* y_perm, int
   k_combine_bwd<<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)dout, (const u32x4*)y_perm, max_rows, pair_row,
                                                      pair_w, topk_idx, T, k, E, vec_per_row, (u32x4*)dy_perm, dw,
                                                      dlogits);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_unrouted_bf16(const int32_t* pair_row, int64_t max_rows, int64_t T, int d, bf16_t* out,
+                                     hipStream_t s) {
+  k_zero_unrouted<<<(unsigned)ceil_div(T, kThreads), kThreads, 0, s>>>(pair_row, max_rows, T, (int64_t)d * 2 / 16,
+                                                                      (u32x4*)out);
   return hipGetLastError();
 }
 

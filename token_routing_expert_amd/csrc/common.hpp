@@ -148,10 +148,13 @@ hipError_t launch_route_project_f32(const float* x, const float* w_router, int T
 constexpr int kPermuteChunk = 512;
 size_t permute_index_workspace(int64_t P, int E);
 // sched (optional): kSchedWords words that the grouping also sets to zero,
-// the tile counters of the grouped products that follow it
+// the tile counters of the grouped products that follow it.
+// row_w (optional): row_w[pair_row[p]] = pair_w[p], each grouped row's
+// routing weight.
 hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E,
                                 int32_t* row_token, int32_t* pair_row, int32_t* expert_offsets,
-                                void* ws, hipStream_t s, int32_t* sched = nullptr);
+                                void* ws, hipStream_t s, int32_t* sched = nullptr,
+                                const float* pair_w = nullptr, float* row_w = nullptr);
 // x_perm[pair_row[t*k+j]] = x[t] for every pair with a row (token-major:
 // each row of x is read once); row_bytes % 16 == 0.
 hipError_t launch_move_rows(const void* x, int64_t T, int k, int64_t row_bytes, const int32_t* pair_row,
@@ -177,9 +180,21 @@ hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, i
 // rows the down projection's k-stages are split over more workgroups and
 // summed there in a fixed order (deterministic).
 size_t split_workspace(int64_t max_rows, int d);
+// One pair per token (k = 1): the down projection can write the layer output
+// itself, out[row_token[r]] = row_w[r] * bf16(y[r]) rounded to bf16 (what
+// the combine computes for a single pair), from its 256-row tiles or its
+// k-split sum; down_scatters says whether the shape takes one of those
+// paths.  Rows of tokens without a pair are not written.
+struct DownScatter {
+  bf16_t* out;               // [T, d]
+  const int32_t* row_token;  // grouped row -> token
+  const float* row_w;        // grouped row -> routing weight
+  int64_t T;
+};
+bool down_scatters(int64_t max_rows, int E, int d, int I, bool have_split_ws);
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws = nullptr,
-                            int32_t* sched = nullptr);
+                            int32_t* sched = nullptr, const DownScatter* sc = nullptr);
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
                               int d, int I, const float* w_gate_up, float* h, hipStream_t s);
 hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
@@ -199,6 +214,10 @@ hipError_t launch_combine_f32(const float* y_perm, int64_t max_rows, const int32
                               const float* pair_w, int64_t T, int k, int d, float* out,
                               hipStream_t s);
 // (pair_w == nullptr: every weight is 1 -- the backward's sum of a token's row gradients)
+// k = 1: out[t] = 0 for every token whose pair has no grouped row (pair_row
+// outside [0, max_rows)); the other rows are left alone
+hipError_t launch_zero_unrouted_bf16(const int32_t* pair_row, int64_t max_rows, int64_t T, int d, bf16_t* out,
+                                     hipStream_t s);
 
 // ---- backward (bf16) ----
 // forward gate/up that also keeps the pre-activations: gu [max_rows, 2I] = [x Wg | x Wu]

@@ -56,6 +56,7 @@ constexpr int kEpiSwiglu = 1;      // Out = silu(A Wg) * (A Wu) (gate/up tiles)
 constexpr int kEpiSwigluSave = 2;  // as kEpiSwiglu, and Out2 = [A Wg | A Wu] (row stride 2N)
 constexpr int kEpiSwigluBwd = 3;   // Out = [dg | du] from dh = A W and Aux = [g | u] (row strides 2N)
 constexpr int kEpiPartial = 4;     // Part[split] = A W over the split's k-stages (float32, row stride N)
+constexpr int kEpiScatter = 5;     // Out[row_token[r]] = row_w[r] * bf16(A W)[r] (one pair per token)
 constexpr int kBwdBlocks = 1;      // column blocks whose g, u the backward epilogue loads together
 
 __device__ __forceinline__ uint2 pack4(const float* f) {
@@ -157,12 +158,14 @@ struct Tile {
 // and its epilogue.  With row_token, the grouped-row -> token map of the
 // next tile is fetched into LDS by DMA one tile ahead, so that entering a
 // tile never waits on a plain global load (which would drain the ring).
+// (launch bounds: workgroup size and waves per SIMD -- OCC workgroups of
+// 2 WM waves per CU need OCC WM / 2 of them, at least one)
 template <int EPI, bool BT, int BK, int OCC, int NJ, int WM, int NS, bool PP>
-__global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
+__global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K, int N, int ldw,
     const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles, const int32_t* __restrict__ row_token,
     int64_t a_rows, bf16_t* __restrict__ Out2, const bf16_t* __restrict__ Aux, int n_split,
-    float* __restrict__ Part, int32_t* __restrict__ sched) {
+    float* __restrict__ Part, int32_t* __restrict__ sched, const float* __restrict__ row_w) {
   // gate/up tiles: 128 gate columns and the matching 128 up columns
   constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   static_assert(!(SWIGLU && BT), "the gate/up weight is only read as [K][2N]");
@@ -174,9 +177,18 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   static_assert(NS >= 3 && NS <= 5, "a ring of 3 to 5 stages");
   static_assert(BM <= 256, "one index DMA covers 256 rows");
   static_assert(!PP || WAVES == 8, "ping-pong pairs two groups of four waves, one wave of each per SIMD");
+  // With kEpiScatter the tile's row -> token map (and row weights) serve
+  // the epilogue, not the activation loads: the activations are the
+  // grouped rows themselves, and the maps are kept for four tiles (the
+  // issue side fetches tile n + 1's while the compute side may still be
+  // finishing tile n - 2).
+  constexpr bool SCATTER = EPI == kEpiScatter;
+  static_assert(!SCATTER || WAVES >= 2, "the row weights are fetched by wave 1");
+  constexpr int NSLOT = SCATTER ? 4 : 2;
   __shared__ __attribute__((aligned(1024))) char sA[NS * GE::A_BYTES];
   __shared__ __attribute__((aligned(1024))) char sB[NS * GE::B_BYTES];
-  __shared__ __attribute__((aligned(1024))) int32_t s_rt[2][256];
+  __shared__ __attribute__((aligned(1024))) int32_t s_rt[NSLOT][256];
+  __shared__ __attribute__((aligned(1024))) float s_rw[SCATTER ? NSLOT : 1][256];
   __shared__ int s_start[kMaxExperts];
   __shared__ int s_mt[kMaxExperts];
   __shared__ int s_lo[kMaxExperts];
@@ -330,12 +342,23 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   const uint32_t b_lds0 = lds_address(sB) + wave * 1024;
 
   // wave 0 copies the token index of grouped rows t.row0 .. t.row0+rows-1
-  // into s_rt[slot] (rows past the tile read as 0 and are never used)
+  // into s_rt[slot] (rows past the tile read as 0 and are never used), and
+  // with SCATTER wave 1 their weights into s_rw[slot]
+  const bool gather = !SCATTER && row_token != nullptr;  // activation row r is token row_token[r]
   auto index_dma = [&](const Tile& t, int slot) {
+    // (bases and sizes through readfirstlane, as in enter: scalar operands)
+    const int bytes = __builtin_amdgcn_readfirstlane(t.rows * 4);
     if (wave == 0) {
       const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(row_token + t.row0), (short)0, t.rows * 4, kBufferConfig);
-      dma16(rs, lds_address(&s_rt[slot][0]), (uint32_t)lane * 16u);
+          __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(row_token + t.row0), (short)0, bytes, kBufferConfig);
+      dma16(rs, __builtin_amdgcn_readfirstlane(lds_address(&s_rt[slot][0])), (uint32_t)lane * 16u);
+    }
+    if constexpr (SCATTER) {
+      if (wave == 1) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(row_w + t.row0), (short)0, bytes, kBufferConfig);
+        dma16(rs, __builtin_amdgcn_readfirstlane(lds_address(&s_rw[slot][0])), (uint32_t)lane * 16u);
+      }
     }
   };
 
@@ -347,12 +370,12 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
   // every lane that loads stays inside its buffer up to the last stage.
   auto enter = [&]() {
     const Tile t = inext;
-    const int slot = i_tile & 1;
+    const int slot = i_tile % NSLOT;
     // (bases and sizes pass through readfirstlane: they are wave-uniform,
     // and saying so keeps the descriptors in scalar registers)
     a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(row_token ? (const void*)A : (const void*)(A + t.row0 * K)), (short)0,
-        __builtin_amdgcn_readfirstlane(row_token ? (int)(a_rows * K * 2) : t.rows * K * 2), kBufferConfig);
+        uniform_ptr(gather ? (const void*)A : (const void*)(A + t.row0 * K)), (short)0,
+        __builtin_amdgcn_readfirstlane(gather ? (int)(a_rows * K * 2) : t.rows * K * 2), kBufferConfig);
     // one expert's weights: [K][ldw] (read transposed by the LDS reads), or
     // with BT [N][K] (rows of k, read like the activations)
     const int64_t w_elems = BT ? (int64_t)N * K : (int64_t)K * ldw;
@@ -363,8 +386,8 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
       const int r = (wave + WAVES * p) * GE::RPI + lane / GE::CPR;
       const int c = (lane % GE::CPR) ^ GE::swz(r);
       int64_t src = r;
-      if (row_token) src = (r < t.rows) ? s_rt[slot][r] : -1;
-      a_voff[p] = (r < t.rows && src >= 0 && src < (row_token ? a_rows : (int64_t)t.rows))
+      if (gather) src = (r < t.rows) ? s_rt[slot][r] : -1;
+      a_voff[p] = (r < t.rows && src >= 0 && src < (gather ? a_rows : (int64_t)t.rows))
                       ? (uint32_t)(src * K + c * 8) * 2u
                       : kOutOfRange;
     }
@@ -401,7 +424,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
     if (u >= 0) {
       inext = decode(u / n_split, i_cursor);
       inext_split = (int)(u % n_split);
-      if (row_token) index_dma(inext, slot ^ 1);
+      if (row_token) index_dma(inext, (i_tile + 1) % NSLOT);
       if (dyn) {
         total += nk;
         if (i_tile + 2 >= rs) claim(i_tile + 2);
@@ -470,7 +493,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
 
   // acc[j][i] holds output row 64 wm + 32 i + lane % 32, columns
   // col_base(j) + 8 q4 + 4 (lane / 32) + {0..3}
-  auto epilogue = [&](const Tile& t, int split) {
+  auto epilogue = [&](const Tile& t, int split, int slot) {
     const int lr = lane % 32, lc = 4 * (lane / 32);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -522,6 +545,27 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
             if (c >= N) continue;
             *(f32x4*)(prow + c) = f32x4{acc[j][i][4 * q4], acc[j][i][4 * q4 + 1], acc[j][i][4 * q4 + 2],
                                         acc[j][i][4 * q4 + 3]};
+          }
+      } else if constexpr (EPI == kEpiScatter) {
+        // the row's token gets the row rounded to bf16 times its routing
+        // weight, rounded again (what the combine computes for one pair)
+        const int tok = s_rt[slot][r];
+        const float wr = s_rw[slot][r];
+        if (tok < 0 || tok >= a_rows) continue;
+        bf16_t* trow = Out + (int64_t)tok * N;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int c = t.n0 + WCOL * wn + 32 * j + 8 * q4 + lc;
+            if (c >= N) continue;
+            float f[4];
+            unpack4(make_uint2(pack_bf16x2(acc[j][i][4 * q4], acc[j][i][4 * q4 + 1]),
+                               pack_bf16x2(acc[j][i][4 * q4 + 2], acc[j][i][4 * q4 + 3])),
+                    f);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) f[v] = fmaf(wr, f[v], 0.f);
+            *(uint2*)(trow + c) = pack4(f);
           }
       } else if constexpr (EPI == kEpiSwigluBwd) {
         // acc is dh; with the saved pre-activations g, u of the row:
@@ -699,7 +743,7 @@ __global__ __launch_bounds__(128 * WM, OCC) void k_grouped_gemm(
       }
       first = 0;
     }
-    epilogue(cur, cur_split);
+    epilogue(cur, cur_split, c_tile % NSLOT);
     zero_acc();
     const int64_t u = unit_of(c_tile + 1);
     if (u < 0) break;
@@ -786,14 +830,14 @@ template <int EPI, bool BT = false, int BK = 32, int OCC = 2, int NJ = 4, int WM
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
                       int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr, int n_split = 1,
-                      float* part = nullptr, int32_t* sched = nullptr) {
+                      float* part = nullptr, int32_t* sched = nullptr, const float* row_w = nullptr) {
   constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   constexpr int BNO = SWIGLU ? 32 * NJ : 64 * NJ;   // output columns per tile
   if (K / BK / n_split < NS - 1) return hipErrorInvalidValue;  // each range spans at least NS - 1 stages
   const int nt = (int)ceil_div(N, BNO);
   dma::k_grouped_gemm<EPI, BT, BK, OCC, NJ, WM, NS, PP>
       <<<persistent_grid(max_rows, E, 64 * WM, nt * n_split, OCC), 128 * WM, 0, s>>>(
-          a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows, out2, aux, n_split, part, sched);
+          a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows, out2, aux, n_split, part, sched, row_w);
   return hipGetLastError();
 }
 
@@ -808,16 +852,33 @@ constexpr int kSplitMax = 8;
 constexpr int kSplitMinStages = 16;
 
 // One thread per 4 columns of a row.
+// With row_token (one pair per token) the rounded row goes, times its
+// routing weight row_w[r] and rounded again, to its token's row of out
+// ([out_rows, N]) instead of row r.
 __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, int n_split,
                                                    const int32_t* __restrict__ offsets, int E, int64_t max_rows,
-                                                   int N, bf16_t* __restrict__ out) {
+                                                   int N, bf16_t* __restrict__ out,
+                                                   const int32_t* __restrict__ row_token,
+                                                   const float* __restrict__ row_w, int64_t out_rows) {
   const int64_t r = blockIdx.y;
   const int c = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
   const int64_t n_rows = clampi<int64_t>(offsets[E], 0, max_rows);
   if (r >= n_rows || c >= N) return;
   f32x4 sum = *(const f32x4*)(part + r * N + c);
   for (int sp = 1; sp < n_split; ++sp) sum += *(const f32x4*)(part + ((int64_t)sp * max_rows + r) * N + c);
-  *(uint2*)(out + r * N + c) = make_uint2(pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3]));
+  const uint2 y = make_uint2(pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3]));
+  if (!row_token) {
+    *(uint2*)(out + r * N + c) = y;
+    return;
+  }
+  const int64_t t = row_token[r];
+  if (t < 0 || t >= out_rows) return;
+  const float w = row_w[r];
+  float f[4];
+  unpack4(y, f);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) f[v] = fmaf(w, f[v], 0.f);
+  *(uint2*)(out + t * N + c) = pack4(f);
 }
 
 // Ranges per tile for a product with few rows (1: no split).  Tiles are
@@ -893,12 +954,22 @@ size_t split_workspace(int64_t max_rows, int d) {
   return max_rows <= kSplitMaxRows ? (size_t)kSplitMax * max_rows * d * sizeof(float) : 0;
 }
 
+int down_split(int64_t max_rows, int E, int d, int I, bool have_split_ws) {
+  if (!have_split_ws || big_tiles(max_rows, E, I)) return 1;
+  return choose_split(max_rows, E, I, d, small_tiles(max_rows, E) ? 64 : 128, 2);
+}
+
+bool down_scatters(int64_t max_rows, int E, int d, int I, bool have_split_ws) {
+  return big_tiles(max_rows, E, I) || down_split(max_rows, E, d, I, have_split_ws) > 1;
+}
+
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws,
-                            int32_t* sched) {
-  if (split_ws != nullptr && !big_tiles(max_rows, E, I)) {
+                            int32_t* sched, const DownScatter* sc) {
+  if (sc && !down_scatters(max_rows, E, d, I, split_ws != nullptr)) return hipErrorInvalidValue;
+  {
     const bool small = small_tiles(max_rows, E);
-    const int n_split = choose_split(max_rows, E, I, d, small ? 64 : 128, 2);
+    const int n_split = down_split(max_rows, E, d, I, split_ws != nullptr);
     if (n_split > 1) {
       const hipError_t e =
           small ? launch_dma<kEpiPartial, false, 32, 2, 4, 1, 3, false>(h, expert_offsets, max_rows, E, I, d, d,
@@ -908,12 +979,18 @@ hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int6
                                           nullptr, nullptr, n_split, split_ws);
       if (e != hipSuccess) return e;
       const dim3 grid((unsigned)ceil_div(d / 4, 256), (unsigned)max_rows);
-      k_split_sum<<<grid, 256, 0, s>>>(split_ws, n_split, expert_offsets, E, max_rows, d, y_perm);
+      k_split_sum<<<grid, 256, 0, s>>>(split_ws, n_split, expert_offsets, E, max_rows, d, sc ? sc->out : y_perm,
+                                       sc ? sc->row_token : nullptr, sc ? sc->row_w : nullptr, sc ? sc->T : 0);
       return hipGetLastError();
     }
   }
+  int32_t* dn_sched = sched ? sched + kSchedDown : nullptr;
+  if (sc)   // 256-row tiles (down_scatters)
+    return launch_dma<kEpiScatter, false, 32, 1, 4, 4, 4, true>(h, expert_offsets, max_rows, E, I, d, d, w_down,
+                                                                 sc->out, s, sc->row_token, sc->T, nullptr, nullptr,
+                                                                 1, nullptr, dn_sched, sc->row_w);
   return launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s, nullptr, 0,
-                                       nullptr, nullptr, sched ? sched + kSchedDown : nullptr);
+                                       nullptr, nullptr, dn_sched);
 }
 
 hipError_t launch_gate_up_save_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,

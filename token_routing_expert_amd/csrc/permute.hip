@@ -105,7 +105,9 @@ __global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __rest
                                                            const int32_t* __restrict__ chunk_base,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ pair_row,
-                                                           int32_t* __restrict__ row_token) {
+                                                           int32_t* __restrict__ row_token,
+                                                           const float* __restrict__ pair_w,
+                                                           float* __restrict__ row_w) {
   __shared__ int running[kMaxExperts];
   __shared__ int s_before[kMaxExperts];
   __shared__ int s_total[kMaxExperts];
@@ -173,7 +175,10 @@ __global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __rest
       int r = running[e] + rank;
       for (int w = 0; w < wave; ++w) r += wave_count[w][e];
       pair_row[p] = r;
-      if (r >= 0 && r < P) row_token[r] = (int32_t)(p / k);
+      if (r >= 0 && r < P) {
+        row_token[r] = (int32_t)(p / k);
+        if (row_w) row_w[r] = pair_w[p];
+      }
     } else if (p < end) {
       pair_row[p] = -1;
     }
@@ -202,7 +207,9 @@ __global__ __launch_bounds__(kSmallThreads) void k_perm_small(const int32_t* __r
                                                                int k, int E, int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ pair_row,
                                                                int32_t* __restrict__ row_token,
-                                                               int32_t* __restrict__ sched) {
+                                                               int32_t* __restrict__ sched,
+                                                               const float* __restrict__ pair_w,
+                                                               float* __restrict__ row_w) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int running[kMaxExperts];
   __shared__ int wave_count[kSmallWaves][kMaxExperts];
@@ -271,7 +278,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_perm_small(const int32_t* __r
       int r = running[e] + rank;
       for (int w = 0; w < wave; ++w) r += wave_count[w][e];
       pair_row[p] = r;
-      if (r >= 0 && r < P) row_token[r] = p / k;
+      if (r >= 0 && r < P) {
+        row_token[r] = p / k;
+        if (row_w) row_w[r] = pair_w[p];
+      }
     } else if (p < P) {
       pair_row[p] = -1;
     }
@@ -335,9 +345,11 @@ size_t permute_index_workspace(int64_t P, int E) {
 constexpr int64_t kSmallPairs = kSmallSteps * kSmallThreads;
 
 hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, int E, int32_t* row_token,
-                                int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s, int32_t* sched) {
+                                int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s, int32_t* sched,
+                                const float* pair_w, float* row_w) {
   if (P <= kSmallPairs) {
-    k_perm_small<<<1, kSmallThreads, 0, s>>>(pair_expert, (int)P, k, E, expert_offsets, pair_row, row_token, sched);
+    k_perm_small<<<1, kSmallThreads, 0, s>>>(pair_expert, (int)P, k, E, expert_offsets, pair_row, row_token, sched,
+                                             pair_w, row_w);
     return hipGetLastError();
   }
   const int n_chunks = (int)ceil_div(P, kPermuteChunk);
@@ -349,7 +361,7 @@ hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, in
     k_perm_scan<<<1, kThreads, 0, s>>>(chunk_count, n_chunks, E, chunk_base, expert_offsets);
   }
   k_perm_scatter<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, k, E, n_chunks, chunk_count, chunk_base,
-                                               expert_offsets, pair_row, row_token);
+                                               expert_offsets, pair_row, row_token, pair_w, row_w);
   return hipGetLastError();
 }
 
