@@ -57,18 +57,36 @@ def test_checker_sees_a_planted_reference():
     assert regs == {208} and other == ["v_add_u32_e32 v1, v208, v2"]
 
 
-@pytest.mark.timeout(600)
-def test_ticket_register_untouched_between_claim_and_post(tmp_path):
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
     src = os.path.join(tre_build.CSRC, "grouped_ffn.hip")
-    out = tmp_path / "grouped_ffn.s"
+    out = tmp_path_factory.mktemp("asm") / "grouped_ffn.s"
     r = subprocess.run([hipcc, *tre_build.FLAGS, "--cuda-device-only", "-S", src, "-o", str(out)],
                        capture_output=True, text=True, timeout=540)
     assert r.returncode == 0, r.stderr[-2000:]
-    refs = ticket_references(out.read_text())
+    return out.read_text()
+
+
+@pytest.mark.timeout(600)
+def test_ticket_register_untouched_between_claim_and_post(gemm_asm):
+    refs = ticket_references(gemm_asm)
     claiming = {k: v for k, v in refs.items() if v[0]}
     assert claiming, "no kernel claims tiles: the claim's instruction pattern changed"
     for name, (regs, other) in claiming.items():
         assert not other, f"{name}: ticket register v{sorted(regs)} also used by {other[:4]}"
+
+
+@pytest.mark.timeout(600)
+def test_gemm_kernels_do_not_spill(gemm_asm):
+    # Spilled registers go through scratch memory: slow in the stage loop,
+    # and scratch loads would join the vector-memory count that the stage
+    # waits rely on.  Every instance of the grouped GEMM keeps all of its
+    # state in registers.
+    kernels = re.findall(r"\.amdhsa_kernel (\S*k_grouped_gemm\S*)\n(.*?)\.end_amdhsa_kernel", gemm_asm, re.S)
+    assert len(kernels) >= 10
+    for name, body in kernels:
+        scratch = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body).group(1))
+        assert scratch == 0, f"{name} spills {scratch} bytes per lane"
