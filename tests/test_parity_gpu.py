@@ -534,6 +534,54 @@ def test_forward_one_pair_per_token_equals_staged(tre, T, d, E, k, I):
     assert rel_l2(to_host(out)[: min(T, 64)], ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T,d,E,k,I", [
+    (4096, 256, 8, 2, 4096),   # gate/up hands out its tail by the ticket counter
+    (2048, 256, 8, 1, 512),    # k = 1: the down projection writes the output rows
+])
+def test_forward_graph_replay_claims_and_row_output(tre, T, d, E, k, I):
+    # The layer captured once as a graph: every replay must zero its tile
+    # counters again (inside the graph, by the grouping kernel) and rewrite
+    # every output row.  Fresh routing is copied in before each replay, with
+    # eager work and synchronisation in between; each replay equals an eager
+    # call bit for bit.
+    torch = _torch()
+    base = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + k, logits="normal_bias")
+    x_g, wgu, wd = to_device(base.x), to_device(base.w_gate_up), to_device(base.w_down)
+    lg_g = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx_g = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w_g = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out_g = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    ws_g = torch.empty(tre.moe_forward_workspace_size(T, d, E, k, I, tre.MOE_BF16), dtype=torch.uint8,
+                       device="cuda")
+    say(f"graph replay T={T} d={d} E={E} k={k} I={I}")
+
+    def layer():
+        tre.moe_forward(x_g, wgu, wd, k, logits=lg_g, topk_idx=idx_g, topk_w=w_g, out=out_g, workspace=ws_g)
+
+    rng = np.random.default_rng(7)
+    lg_g.copy_(to_device(base.logits))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    sync()
+    for rep in range(3):
+        lg_g.copy_(to_device(rng.normal(size=(T, E)).astype(np.float32)))
+        out_g.fill_(float("nan"))
+        sync()
+        graph.replay()
+        sync()
+        replayed = out_g.clone()
+        eager, _, _ = tre.moe_forward(x_g, wgu, wd, k, logits=lg_g)
+        sync()
+        assert torch.equal(replayed.view(torch.int16), eager.view(torch.int16)), rep
+
+
 def test_forward_all_tokens_one_expert(tre):
     inp = workloads.make_custom(T=700, d=128, E=4, k=1, I=128, dtype="bf16", seed=9, logits="normal")
     inp.logits[:, 2] += 100.0
