@@ -36,7 +36,10 @@
 //     offsets (no host synchronisation) and walks it round-robin; tiles are
 //     ordered expert, then column tile, then row tile, and consecutive tiles
 //     go to workgroups of one XCD, so the row tiles that share a weight slice
-//     run together on one L2.
+//     run together on one L2; with four or more rounds of 256-row tiles the
+//     last round and a half is handed out by an atomic ticket counter;
+//   * with one pair per token the down projection can write the layer
+//     output rows itself (routing weight applied, as the combine would).
 // float32 path: plain per-element dot products (small, for the float32
 // workloads).
 #include "common.hpp"
