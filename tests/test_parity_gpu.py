@@ -493,6 +493,7 @@ def test_forward_claimed_tail_equals_dealt_tiles(tre, T, d, E, k, I):
 
 @pytest.mark.parametrize("T,d,E,k,I", [
     (2048, 256, 8, 1, 512),    # 256-row tiles: the down projection writes the output rows
+    (16384, 4096, 8, 1, 256),  # ... with over 1000 tiles: and hands out its tail by the ticket counter
     (64, 512, 16, 1, 1024),    # few rows: the k-split sum writes the output rows
     (300, 256, 8, 1, 256),     # neither: grouped rows, then the combine
     (2048, 256, 8, 2, 512),    # k = 2: always the combine
