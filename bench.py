@@ -5,17 +5,24 @@ A step is one pass of the whole hot path over one batch of synthetic input,
 with every input already resident in HBM: route (top-k + renormalised
 softmax) -> permute (group pairs by expert) -> gate/up projection with
 SwiGLU, reading the token rows in place -> down projection -> combine: the
-same kernels moe_forward launches.  Each stage is one C-ABI call of
-libmoe.so on torch's current stream; HIP events on that stream bracket every
-stage, so each stage's average duration is measured live over the timed
-region.  The headline (value, ms_per_step) times the same K steps through the
-fused entry point moe_forward, which launches these kernels back to back.
+kernels the fused entry point moe_forward launches.
+
+Timing is HBM-honest: before every timed step a scratch buffer larger than
+the 256 MB Infinity Cache (512 MiB by default) is written on the same stream,
+so no operand of the step is served from a cache left warm by the step
+before; HIP events on the stream bracket the step itself (not the flush).
+The headline (value, ms_per_step) is K such steps through moe_forward; the
+same K steps run again as separate C-ABI calls with events between the
+stages, which gives every kernel's average duration; a warm figure (steps
+back to back, no flush) is reported beside it.
 
 Prints ONE JSON line.  ``value`` = routed (token, expert) pairs per second of
-the whole layer (moe_forward).  ``roofline`` describes the dominant kernel (the gate/up
-grouped GEMM: algorithmic flops per launch / measured launch duration against
-the MI355X dense bf16 MFMA peak).  ``cpu_baseline`` is the CPU oracle timed on
-a bounded sample of the same workload on this host.
+the whole layer.  ``roofline`` describes the dominant kernel, the gate/up
+grouped GEMM: its algorithmic bytes and flops per launch against its
+measured launch duration, taken against the bound its arithmetic intensity
+puts it under (HBM below the ridge point of 2500 TFLOP/s / 8 TB/s, MFMA
+above), with the other fraction beside it.  ``cpu_baseline`` is the CPU
+oracle timed on a bounded sample of the same workload on this host.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -92,6 +99,25 @@ def algorithmic_work(inp, n_rows: int, live_experts: int):
     }
 
 
+def host_cpu():
+    """What the host offers the oracle: the CPU model, the logical CPUs the
+    machine reports and the ones this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count() or 1
+    return {"cpu_model": model, "host_cpus": os.cpu_count() or 1, "allowed_cpus": allowed}
+
+
 def cpu_baseline(inp, seconds: float):
     """Time the CPU oracle on a bounded sample of the workload."""
     import oracle
@@ -116,6 +142,7 @@ def cpu_baseline(inp, seconds: float):
     t_ffn = time.perf_counter() - t0
     # the index work is charged in proportion to the sample
     t_total = t_ffn + t_index * n / inp.T
+    host = host_cpu()
     return {
         "value": n * inp.k / t_total,
         "unit": "pairs/s",
@@ -123,15 +150,237 @@ def cpu_baseline(inp, seconds: float):
         "kind": "oracle",
         "sample": f"{n} of {inp.T} tokens ({n * inp.k} pairs) through experts+combine in float64, "
                   f"plus route+dispatch over all tokens charged pro rata; {t_total:.1f} s",
+        **host,
+        "thread_cap": f"{oracle.THREAD_CAP} threads at most: the CPU share one GPU is given on a shared "
+                      f"multi-GPU host; here {threads} of {host['allowed_cpus']} allowed CPUs",
     }
+
+
+class Layer:
+    """One workload resident on the GPU, with raw C-ABI calls whose pointers
+    are marshalled once."""
+
+    def __init__(self, lib, tre, torch, inp):
+        self.lib, self.torch, self.inp = lib, torch, inp
+        T, d, E, k, I = inp.T, inp.d, inp.E, inp.k, inp.I
+        P = T * k
+        self.P = P
+        dev_dtype = torch.float32 if inp.dtype == "f32" else torch.bfloat16
+        self.dev_dtype = dev_dtype
+        dt = tre.MOE_F32 if inp.dtype == "f32" else tre.MOE_BF16
+        self.dt = dt
+        self.x = to_device(inp.x, torch)
+        self.wgu = to_device(inp.w_gate_up, torch)
+        self.wd = to_device(inp.w_down, torch)
+        if inp.logits is not None:
+            self.logits = to_device(inp.logits, torch)
+            self.topk_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            self.topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        else:
+            self.logits = None
+            self.topk_idx = to_device(inp.pair_expert.reshape(T, k), torch)
+            self.topk_w = to_device(inp.pair_w.reshape(T, k), torch)
+        gather_off = inp.dtype == "f32"
+        self.x_perm = torch.empty((P, d), dtype=dev_dtype, device="cuda") if gather_off else None
+        self.row_token = torch.empty(P, dtype=torch.int32, device="cuda")
+        self.pair_row = torch.empty(P, dtype=torch.int32, device="cuda")
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        self.h = torch.empty((P, I), dtype=dev_dtype, device="cuda")
+        self.y_perm = torch.empty((P, d), dtype=dev_dtype, device="cuda")
+        self.out = torch.empty((T, d), dtype=dev_dtype, device="cuda")
+        self.pws_bytes = lib.moe_permute_workspace_size(T, k, E)
+        self.pws = torch.empty(max(self.pws_bytes, 1), dtype=torch.uint8, device="cuda")
+        self.fws_bytes = lib.moe_forward_workspace_size(T, d, E, k, I, dt)
+        self.fws = torch.empty(max(self.fws_bytes, 1), dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.current_stream()
+        sp = self.stream.cuda_stream
+        ptr = self.ptr
+        self.calls = {
+            "route": (lambda: lib.moe_route_topk(ptr(self.logits), T, E, k, ptr(self.topk_idx), ptr(self.topk_w),
+                                                 sp)) if self.logits is not None else (lambda: 0),
+            # bf16: the index only, then the projection reads token rows in
+            # place (what moe_forward does); float32: rows are moved
+            "permute": lambda: lib.moe_permute(ptr(self.x), dt, T, d, k, ptr(self.topk_idx), E,
+                                               ptr(self.x_perm) if gather_off else None, ptr(self.row_token),
+                                               ptr(self.pair_row), ptr(self.offsets), ptr(self.pws), self.pws_bytes,
+                                               sp),
+            "gate_up": lambda: lib.moe_gate_up_swiglu(ptr(self.x_perm) if gather_off else ptr(self.x),
+                                                      ptr(self.offsets), P, E, d, I, ptr(self.wgu), dt,
+                                                      None if gather_off else ptr(self.row_token), T, ptr(self.h),
+                                                      sp),
+            "down": lambda: lib.moe_down_proj(ptr(self.h), ptr(self.offsets), P, E, d, I, ptr(self.wd), dt,
+                                              ptr(self.y_perm), sp),
+            "combine": lambda: lib.moe_combine(ptr(self.y_perm), P, ptr(self.pair_row), ptr(self.topk_w), T, k, d,
+                                               dt, ptr(self.out), sp),
+        }
+
+    @staticmethod
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    def fused(self, stream=None):
+        inp, ptr = self.inp, self.ptr
+        sp = (stream or self.stream).cuda_stream
+        st = self.lib.moe_forward(ptr(self.x), ptr(self.logits), inp.T, inp.d, inp.E, inp.k, inp.I, ptr(self.wgu),
+                                  ptr(self.wd), self.dt, ptr(self.topk_idx), ptr(self.topk_w), None, None, None,
+                                  ptr(self.out), ptr(self.fws), self.fws_bytes, sp)
+        if st != 0:
+            raise RuntimeError(f"moe_forward failed with status {st}")
+
+    def staged(self, events=None):
+        for i, name in enumerate(STAGES):
+            if events is not None:
+                events[i].record(self.stream)
+            st = self.calls[name]()
+            if st != 0:
+                raise RuntimeError(f"{name} failed with status {st}")
+        if events is not None:
+            events[len(STAGES)].record(self.stream)
+
+
+class Flush:
+    """Writes a scratch buffer larger than the Infinity Cache on the stream,
+    so that the next step reads its operands from HBM."""
+
+    def __init__(self, torch, mib: int):
+        self.buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda") if mib > 0 else None
+        self.v = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.v = (self.v + 1) & 0xFF
+            self.buf.fill_(self.v)
+
+
+def time_layer(torch, layer, flush, steps: int, warmup: int):
+    """Cold steps through moe_forward (flush, event, layer, event) and the
+    same steps staged, with events between the kernels; then warm steps back
+    to back.  Returns the timings in ms."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    stream = layer.stream
+    for _ in range(warmup):
+        flush()
+        layer.staged()
+        flush()
+        layer.fused()
+    torch.cuda.synchronize()
+
+    # cold fused steps: exactly `steps` of them, synchronised on both sides
+    pairs = [(ev(), ev()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in pairs:
+        flush()
+        a.record(stream)
+        layer.fused()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_with_flush = (time.perf_counter() - t0) * 1e3 / steps
+    cold = [a.elapsed_time(b) for a, b in pairs]
+
+    # cold staged steps (per-kernel durations)
+    evs = [[ev() for _ in range(len(STAGES) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for st in range(steps):
+        flush()
+        layer.staged(evs[st])
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([evs[st][i].elapsed_time(evs[st][i + 1]) for st in range(steps)]))
+                for i, name in enumerate(STAGES)}
+    staged_ms = float(np.mean([evs[st][0].elapsed_time(evs[st][len(STAGES)]) for st in range(steps)]))
+
+    # warm steps back to back (operands partly cache-resident)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.fused()
+    torch.cuda.synchronize()
+    warm = (time.perf_counter() - t0) * 1e3 / steps
+    return {"cold_ms": float(np.mean(cold)), "cold_min_ms": float(np.min(cold)),
+            "cold_median_ms": float(np.median(cold)), "wall_ms_with_flush": wall_with_flush,
+            "warm_ms": warm, "stage_ms": stage_ms, "staged_ms": staged_ms}
+
+
+def kernel_table(inp, stage_ms, n_rows, live):
+    work = algorithmic_work(inp, n_rows, live)
+    peak_mm = PEAK_F32_TFLOPS if inp.dtype == "f32" else PEAK_BF16_TFLOPS
+    kernels = {}
+    for name in STAGES:
+        ms = stage_ms[name]
+        w = work[name]
+        ent = {"ms": round(ms, 5)}
+        if ms > 0 and w.get("bytes"):
+            ent["gbs"] = round(w["bytes"] / (ms * 1e-3) / 1e9, 1)
+            ent["hbm_frac"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+        if ms > 0 and w.get("flops"):
+            ent["tflops"] = round(w["flops"] / (ms * 1e-3) / 1e12, 1)
+            ent["mfma_frac"] = round(ent["tflops"] / peak_mm, 4)
+        kernels[name] = ent
+    return kernels, work, peak_mm
+
+
+def roofline_of(inp, kernels, work, peak_mm, workload):
+    """The dominant kernel (gate/up) against the bound its arithmetic
+    intensity puts it under."""
+    gu = kernels["gate_up"]
+    w = work["gate_up"]
+    ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ai = w["flops"] / w["bytes"] if w["bytes"] else float("inf")
+    traffic = None
+    rec = read_traffic_record(workload)
+    if rec is not None and rec.get("source_sha256_16") == kernel_source_hash():
+        traffic = float(rec["hbm_bytes_per_launch"])
+    kernel = ("gate/up grouped GEMM + SwiGLU (dma::k_grouped_gemm<1, false, ...>, tile shape chosen per call)"
+              if inp.dtype == "bf16" else "gate/up grouped FFN (k_ffn_gate_up_f32)")
+    common = {"kernel": kernel, "traffic": traffic, "flops_per_launch": w["flops"], "bytes_per_launch": w["bytes"],
+              "arithmetic_intensity": round(ai, 1), "ridge": round(ridge, 1), "launch_ms": gu["ms"]}
+    if ai < ridge:
+        return {"bound": "hbm", "achieved": gu.get("gbs"), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gu.get("hbm_frac"), **common,
+                "mfma": {"achieved": gu.get("tflops"), "peak": peak_mm, "unit": "TFLOP/s",
+                         "frac": gu.get("mfma_frac")}}
+    return {"bound": "mfma", "achieved": gu.get("tflops"), "peak": peak_mm, "unit": "TFLOP/s",
+            "frac": gu.get("mfma_frac"), **common,
+            "hbm": {"achieved": gu.get("gbs"), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gu.get("hbm_frac")}}
+
+
+def routed(torch, layer):
+    E = layer.inp.E
+    n_rows = int(layer.offsets[E].item())
+    counts = (layer.offsets[1:] - layer.offsets[:-1]).cpu().numpy()
+    return n_rows, int((counts > 0).sum())
+
+
+def measure_extra(lib, tre, torch, name, flush, steps, warmup):
+    """The layer and its kernels on another workload (cold), for the line."""
+    inp = workloads.make(name)
+    layer = Layer(lib, tre, torch, inp)
+    t = time_layer(torch, layer, flush, steps, warmup)
+    n_rows, live = routed(torch, layer)
+    kernels, work, peak_mm = kernel_table(inp, t["stage_ms"], n_rows, live)
+    res = {"ms_per_step": round(t["cold_ms"], 5), "pairs_per_s": layer.P / (t["cold_ms"] * 1e-3),
+           "warm_ms_per_step": round(t["warm_ms"], 5), "roofline": roofline_of(inp, kernels, work, peak_mm, name),
+           "kernels": kernels}
+    del layer
+    torch.cuda.empty_cache()
+    return res
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=workloads.ORDER[1], choices=workloads.ORDER)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large_e128", choices=workloads.ORDER,
+                    help="the headline workload (default: the largest single-GPU one, the whole layer with "
+                         "128 experts)")
+    ap.add_argument("--extra", default="small_bf16",
+                    help="comma-separated workloads measured beside the headline (cold layer and kernels), "
+                         "or 'none'")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="MiB of scratch written before every timed step (0: no flush)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the router projection, permute-with-rows, graph and backward measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -150,65 +399,14 @@ def main() -> int:
     inp = workloads.make(args.workload)
     T, d, E, k, I = inp.T, inp.d, inp.E, inp.k, inp.I
     P = T * k
-    dev_dtype = torch.float32 if inp.dtype == "f32" else torch.bfloat16
-    dt = tre.MOE_F32 if inp.dtype == "f32" else tre.MOE_BF16
-
-    x = to_device(inp.x, torch)
-    wgu = to_device(inp.w_gate_up, torch)
-    wd = to_device(inp.w_down, torch)
-    if inp.logits is not None:
-        logits = to_device(inp.logits, torch)
-        topk_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-        topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    else:
-        logits = None
-        topk_idx = to_device(inp.pair_expert.reshape(T, k), torch)
-        topk_w = to_device(inp.pair_w.reshape(T, k), torch)
-    gather_off = inp.dtype == "f32"
-    x_perm = torch.empty((P, d), dtype=dev_dtype, device="cuda") if gather_off else None
-    row_token = torch.empty(P, dtype=torch.int32, device="cuda")
-    pair_row = torch.empty(P, dtype=torch.int32, device="cuda")
-    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    h = torch.empty((P, I), dtype=dev_dtype, device="cuda")
-    y_perm = torch.empty((P, d), dtype=dev_dtype, device="cuda")
-    out = torch.empty((T, d), dtype=dev_dtype, device="cuda")
-    pws_bytes = lib.moe_permute_workspace_size(T, k, E)
-    pws = torch.empty(max(pws_bytes, 1), dtype=torch.uint8, device="cuda")
-    fws_bytes = lib.moe_forward_workspace_size(T, d, E, k, I, dt)
-    fws = torch.empty(max(fws_bytes, 1), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
+    layer = Layer(lib, tre, torch, inp)
+    stream = layer.stream
     sp = stream.cuda_stream
-
-    def ptr(t):
-        return None if t is None else t.data_ptr()
-
-    # raw C-ABI calls with the pointers marshalled once
-    calls = {
-        "route": (lambda: lib.moe_route_topk(ptr(logits), T, E, k, ptr(topk_idx), ptr(topk_w), sp))
-        if logits is not None else (lambda: 0),
-        # bf16: the index only, then the projection reads token rows in place
-        # (what moe_forward does); float32: rows are moved
-        "permute": lambda: lib.moe_permute(ptr(x), dt, T, d, k, ptr(topk_idx), E, ptr(x_perm) if gather_off else None,
-                                           ptr(row_token), ptr(pair_row), ptr(offsets), ptr(pws), pws_bytes, sp),
-        "gate_up": lambda: lib.moe_gate_up_swiglu(ptr(x_perm) if gather_off else ptr(x), ptr(offsets), P, E, d, I,
-                                                  ptr(wgu), dt, None if gather_off else ptr(row_token), T, ptr(h), sp),
-        "down": lambda: lib.moe_down_proj(ptr(h), ptr(offsets), P, E, d, I, ptr(wd), dt, ptr(y_perm), sp),
-        "combine": lambda: lib.moe_combine(ptr(y_perm), P, ptr(pair_row), ptr(topk_w), T, k, d, dt, ptr(out), sp),
-    }
-
-    def fused():
-        return lib.moe_forward(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(topk_idx),
-                               ptr(topk_w), None, None, None, ptr(out), ptr(fws), fws_bytes, sp)
-
-    def run_step(events=None):
-        for i, name in enumerate(STAGES):
-            if events is not None:
-                events[i].record(stream)
-            st = calls[name]()
-            if st != 0:
-                raise RuntimeError(f"{name} failed with status {st}")
-        if events is not None:
-            events[len(STAGES)].record(stream)
+    dev_dtype, dt = layer.dev_dtype, layer.dt
+    ptr = layer.ptr
+    x, wgu, wd, logits = layer.x, layer.wgu, layer.wd, layer.logits
+    topk_idx, topk_w = layer.topk_idx, layer.topk_w
+    flush = Flush(torch, args.flush_mb)
 
     if args.copy_calibration_mb > 0:
         # a device-to-device copy of known size whose source is not cache
@@ -216,230 +414,157 @@ def main() -> int:
         n = args.copy_calibration_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty(n, dtype=torch.uint8, device="cuda")
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         src.fill_(1)
-        flush.fill_(2)
+        big.fill_(2)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst, flush
-    def run_fused():
-        st = fused()
-        if st != 0:
-            raise RuntimeError(f"moe_forward failed with status {st}")
+        del src, dst, big
 
-    for _ in range(args.warmup):
-        run_step()
-        run_fused()
-    torch.cuda.synchronize()
-    n_rows = int(offsets[E].item())
-    counts = (offsets[1:] - offsets[:-1]).cpu().numpy()
-    live = int((counts > 0).sum())
+    # ---- timed regions 1 and 2: K cold layer steps through moe_forward (the
+    # headline), then the same K steps staged with events between kernels ----
+    t = time_layer(torch, layer, flush, args.steps, args.warmup)
+    ms_per_step = t["cold_ms"]
+    n_rows, live = routed(torch, layer)
+    kernels, work, peak_mm = kernel_table(inp, t["stage_ms"], n_rows, live)
+    roofline = roofline_of(inp, kernels, work, peak_mm, args.workload)
 
-    # ---- timed region 1 (the headline): exactly K layer steps through the
-    # fused entry point moe_forward ----
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_fused()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # ---- timed region 2: the same K steps as separate C-ABI calls with HIP
-    # events on the stream around every stage (per-stage durations, roofline)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for st in range(args.steps):
-        run_step(evs[st])
-    torch.cuda.synchronize()
-    staged_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    stage_ms = {name: float(np.mean([evs[st][i].elapsed_time(evs[st][i + 1]) for st in range(args.steps)]))
-                for i, name in enumerate(STAGES)}
-    gpu_ms = float(np.mean([evs[st][0].elapsed_time(evs[st][len(STAGES)]) for st in range(args.steps)]))
-
-    # ---- timed region 2b: the same layer captured once as a HIP graph and
-    # replayed K times (what a decode loop would do; the library records no
-    # host work, so the whole layer is one graph) ----
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
-        st = lib.moe_forward(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(topk_idx),
-                             ptr(topk_w), None, None, None, ptr(out), ptr(fws), fws_bytes, cap.cuda_stream)
-        if st != 0:
-            raise RuntimeError(f"moe_forward (captured) failed with status {st}")
-    for _ in range(args.warmup):
-        graph.replay()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    g0.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1) / args.steps
-    del graph
-
-    # ---- timed region 2c: the permutation with its row moves (moe_permute
-    # with x_perm), the step as the benchmark defines it: each token row read
-    # once and written to its k grouped rows, plus the index arrays.  The
-    # fused bf16 layer skips the row copy (its gate/up reads token rows in
-    # place), so this is reported beside the layer.
-    xp_rows = torch.empty((P, d), dtype=dev_dtype, device="cuda")
-    pr_tok = torch.empty(P, dtype=torch.int32, device="cuda")
-    pr_row = torch.empty(P, dtype=torch.int32, device="cuda")
-    pr_off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-
-    def run_permute_rows():
-        st = lib.moe_permute(ptr(x), dt, T, d, k, ptr(topk_idx), E, ptr(xp_rows), ptr(pr_tok), ptr(pr_row),
-                             ptr(pr_off), ptr(pws), pws_bytes, sp)
-        if st != 0:
-            raise RuntimeError(f"moe_permute failed with status {st}")
-    for _ in range(args.warmup):
-        run_permute_rows()
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    p0.record(stream)
-    for _ in range(args.steps):
-        run_permute_rows()
-    p1.record(stream)
-    torch.cuda.synchronize()
-    pr_ms = p0.elapsed_time(p1) / args.steps
-    s_elem = 4 if inp.dtype == "f32" else 2
-    pr_bytes = T * d * s_elem * (1 + k) + 16 * P
-    permute_rows = {"ms": round(pr_ms, 5), "bytes_per_call": pr_bytes,
-                    "gbs": round(pr_bytes / (pr_ms * 1e-3) / 1e9, 1),
-                    "hbm_frac": round(pr_bytes / (pr_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del xp_rows
-
-    # ---- timed region 3 (reported beside the layer, not part of it): the
-    # router projection fused with routing, x @ W_r^T then top-k, on the
-    # workload's tokens and a seeded router weight [E, d] ----
-    router = None
-    if logits is not None:
-        w_r = to_device(workloads.router_weight(inp), torch)
-        r_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-        r_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-
-        def run_router():
-            st = lib.moe_route_project(ptr(x), ptr(w_r), dt, T, d, E, k, None, ptr(r_idx), ptr(r_w), sp)
-            if st != 0:
-                raise RuntimeError(f"moe_route_project failed with status {st}")
+    graph_ms = permute_rows = router = backward = None
+    if not args.no_extras:
+        # ---- timed region 3: the same layer captured once as a HIP graph and
+        # replayed K times back to back (what a decode loop would do; the
+        # library records no host work, so the whole layer is one graph) ----
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            layer.fused(stream=cap)
         for _ in range(args.warmup):
-            run_router()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            graph.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        ev0.record(stream)
+        g0.record(stream)
         for _ in range(args.steps):
-            run_router()
-        ev1.record(stream)
+            graph.replay()
+        g1.record(stream)
         torch.cuda.synchronize()
-        r_ms = ev0.elapsed_time(ev1) / args.steps
-        s_el = 4 if inp.dtype == "f32" else 2
-        r_bytes = T * d * s_el + E * d * s_el + 8 * T * k
-        r_flops = 2 * T * d * E
-        router = {"ms": round(r_ms, 5), "bound": "hbm", "bytes_per_launch": r_bytes,
-                  "gbs": round(r_bytes / (r_ms * 1e-3) / 1e9, 1),
-                  "hbm_frac": round(r_bytes / (r_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                  "tflops": round(r_flops / (r_ms * 1e-3) / 1e12, 2)}
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del graph
 
-    # ---- timed region 4 (reported beside the layer): the layer's backward
-    # pass, moe_backward, which recomputes the forward it needs ----
-    backward = None
-    if inp.dtype == "bf16":
-        rng = np.random.default_rng([inp_seed(args.workload), 99])
-        dout = to_device(workloads.bf16_bits(rng.normal(size=(T, d)).astype(np.float32)), torch)
-        gdx = torch.empty((T, d), dtype=dev_dtype, device="cuda")
-        gwgu = torch.empty((E, d, 2 * I), dtype=dev_dtype, device="cuda")
-        gwd = torch.empty((E, I, d), dtype=dev_dtype, device="cuda")
-        gtw = torch.empty((T, k), dtype=torch.float32, device="cuda")
-        glg = torch.empty((T, E), dtype=torch.float32, device="cuda") if logits is not None else None
-        b_idx = torch.empty((T, k), dtype=torch.int32, device="cuda") if logits is not None else topk_idx
-        b_w = torch.empty((T, k), dtype=torch.float32, device="cuda") if logits is not None else topk_w
-        bws_bytes = lib.moe_backward_workspace_size(T, d, E, k, I, dt)
-        bws = torch.empty(max(bws_bytes, 1), dtype=torch.uint8, device="cuda")
-
-        def run_backward(recompute=1):
-            st = lib.moe_backward(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(b_idx), ptr(b_w),
-                                  ptr(dout), ptr(gdx), ptr(gwgu), ptr(gwd), ptr(gtw), ptr(glg), recompute, ptr(bws),
-                                  bws_bytes, sp)
-            if st != 0:
-                raise RuntimeError(f"moe_backward failed with status {st}")
-
-        def run_forward_train():
-            st = lib.moe_forward_train(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(b_idx),
-                                       ptr(b_w), ptr(gout), ptr(bws), bws_bytes, sp)
-            if st != 0:
-                raise RuntimeError(f"moe_forward_train failed with status {st}")
-        gout = torch.empty((T, d), dtype=dev_dtype, device="cuda")
-
-        def timed(fn, n):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        def timed_cold(fn, n):
+            # n cold calls: flush, event, call, event
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
             torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(n):
+            for a, b in pairs:
+                flush()
+                a.record(stream)
                 fn()
-            e1.record(stream)
+                b.record(stream)
             torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / n
-        for _ in range(args.warmup):
-            run_backward()
-        b_ms = timed(run_backward, args.steps)
-        # a training step: the forward that keeps its intermediates, then the
-        # backward from them (events around the pair, and around each)
-        for _ in range(args.warmup):
-            run_forward_train()
-            run_backward(0)
-        step_ms = timed(lambda: (run_forward_train(), run_backward(0)), args.steps)
-        ft_ms = timed(run_forward_train, args.steps)
-        bs_ms = timed(lambda: run_backward(0), args.steps)
-        # matrix products per call: the recomputed forward (6 n d I) and the
-        # gradients (dh 2, dW_down 2, dx 4, dW_gate_up 4: 12 n d I)
-        b_flops = 18 * n_rows * d * I
-        backward = {"ms": round(b_ms, 5), "flops_per_call": b_flops,
-                    "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 1),
-                    "mfma_frac": round(b_flops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                    "pairs_per_s": P / (b_ms * 1e-3),
-                    # training step: 6 n d I (forward) + 12 n d I (gradients), no recompute
-                    "training_step": {"ms": round(step_ms, 5), "forward_train_ms": round(ft_ms, 5),
-                                      "backward_saved_ms": round(bs_ms, 5),
-                                      "tflops": round(18 * n_rows * d * I / (step_ms * 1e-3) / 1e12, 1),
-                                      "pairs_per_s": P / (step_ms * 1e-3)}}
-        del gdx, gwgu, gwd, bws, gout
+            return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
 
-    work = algorithmic_work(inp, n_rows, live)
-    peak_mm = PEAK_F32_TFLOPS if inp.dtype == "f32" else PEAK_BF16_TFLOPS
-    kernels = {}
-    for name in STAGES:
-        ms = stage_ms[name]
-        w = work[name]
-        ent = {"ms": round(ms, 5)}
-        if ms > 0 and w.get("bytes"):
-            ent["gbs"] = round(w["bytes"] / (ms * 1e-3) / 1e9, 1)
-            ent["hbm_frac"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
-        if ms > 0 and w.get("flops"):
-            ent["tflops"] = round(w["flops"] / (ms * 1e-3) / 1e12, 1)
-            ent["mfma_frac"] = round(ent["tflops"] / peak_mm, 4)
-        kernels[name] = ent
+        # ---- timed region 4: the permutation with its row moves (moe_permute
+        # with x_perm), the step as the benchmark defines it: each token row
+        # read once and written to its k grouped rows, plus the index arrays.
+        # The fused bf16 layer skips the row copy (its gate/up reads token rows
+        # in place), so this is reported beside the layer.
+        xp_rows = torch.empty((P, d), dtype=dev_dtype, device="cuda")
+        pr_tok = torch.empty(P, dtype=torch.int32, device="cuda")
+        pr_row = torch.empty(P, dtype=torch.int32, device="cuda")
+        pr_off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
 
-    gu = kernels["gate_up"]
-    traffic = None
-    rec = read_traffic_record(args.workload)
-    if rec is not None and rec.get("source_sha256_16") == kernel_source_hash():
-        traffic = float(rec["hbm_bytes_per_launch"])
-    roofline = {
-        "bound": "mfma",
-        "kernel": "gate/up grouped GEMM + SwiGLU (dma::k_grouped_gemm<1, false, ...>, tile shape chosen per call)" if inp.dtype == "bf16"
-                  else "gate/up grouped FFN (k_ffn_gate_up_f32)",
-        "achieved": gu.get("tflops"),
-        "peak": peak_mm,
-        "unit": "TFLOP/s",
-        "frac": gu.get("mfma_frac"),
-        "traffic": traffic,
-        "flops_per_launch": work["gate_up"]["flops"],
-        "launch_ms": gu["ms"],
-    }
+        def run_permute_rows():
+            st = lib.moe_permute(ptr(x), dt, T, d, k, ptr(topk_idx), E, ptr(xp_rows), ptr(pr_tok), ptr(pr_row),
+                                 ptr(pr_off), ptr(layer.pws), layer.pws_bytes, sp)
+            if st != 0:
+                raise RuntimeError(f"moe_permute failed with status {st}")
+        for _ in range(args.warmup):
+            run_permute_rows()
+        pr_ms = timed_cold(run_permute_rows, args.steps)
+        s_elem = 4 if inp.dtype == "f32" else 2
+        pr_bytes = T * d * s_elem * (1 + k) + 16 * P
+        permute_rows = {"ms": round(pr_ms, 5), "bytes_per_call": pr_bytes,
+                        "gbs": round(pr_bytes / (pr_ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(pr_bytes / (pr_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del xp_rows
+
+        # ---- timed region 5 (beside the layer, not part of it): the router
+        # projection fused with routing, x @ W_r^T then top-k, on the
+        # workload's tokens and a seeded router weight [E, d] ----
+        if logits is not None:
+            w_r = to_device(workloads.router_weight(inp), torch)
+            r_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            r_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+
+            def run_router():
+                st = lib.moe_route_project(ptr(x), ptr(w_r), dt, T, d, E, k, None, ptr(r_idx), ptr(r_w), sp)
+                if st != 0:
+                    raise RuntimeError(f"moe_route_project failed with status {st}")
+            for _ in range(args.warmup):
+                run_router()
+            r_ms = timed_cold(run_router, args.steps)
+            s_el = 4 if inp.dtype == "f32" else 2
+            r_bytes = T * d * s_el + E * d * s_el + 8 * T * k
+            r_flops = 2 * T * d * E
+            router = {"ms": round(r_ms, 5), "bound": "hbm", "bytes_per_launch": r_bytes,
+                      "gbs": round(r_bytes / (r_ms * 1e-3) / 1e9, 1),
+                      "hbm_frac": round(r_bytes / (r_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "tflops": round(r_flops / (r_ms * 1e-3) / 1e12, 2)}
+
+        # ---- timed region 6 (beside the layer): the layer's backward pass,
+        # moe_backward, which recomputes the forward it needs, and a training
+        # step (the forward that keeps its intermediates, then the backward
+        # from them) ----
+        if inp.dtype == "bf16":
+            rng = np.random.default_rng([inp_seed(args.workload), 99])
+            dout = to_device(workloads.bf16_bits(rng.normal(size=(T, d)).astype(np.float32)), torch)
+            gdx = torch.empty((T, d), dtype=dev_dtype, device="cuda")
+            gwgu = torch.empty((E, d, 2 * I), dtype=dev_dtype, device="cuda")
+            gwd = torch.empty((E, I, d), dtype=dev_dtype, device="cuda")
+            gtw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+            glg = torch.empty((T, E), dtype=torch.float32, device="cuda") if logits is not None else None
+            b_idx = torch.empty((T, k), dtype=torch.int32, device="cuda") if logits is not None else topk_idx
+            b_w = torch.empty((T, k), dtype=torch.float32, device="cuda") if logits is not None else topk_w
+            bws_bytes = lib.moe_backward_workspace_size(T, d, E, k, I, dt)
+            bws = torch.empty(max(bws_bytes, 1), dtype=torch.uint8, device="cuda")
+            gout = torch.empty((T, d), dtype=dev_dtype, device="cuda")
+
+            def run_backward(recompute=1):
+                st = lib.moe_backward(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(b_idx),
+                                      ptr(b_w), ptr(dout), ptr(gdx), ptr(gwgu), ptr(gwd), ptr(gtw), ptr(glg),
+                                      recompute, ptr(bws), bws_bytes, sp)
+                if st != 0:
+                    raise RuntimeError(f"moe_backward failed with status {st}")
+
+            def run_forward_train():
+                st = lib.moe_forward_train(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(b_idx),
+                                           ptr(b_w), ptr(gout), ptr(bws), bws_bytes, sp)
+                if st != 0:
+                    raise RuntimeError(f"moe_forward_train failed with status {st}")
+
+            for _ in range(args.warmup):
+                run_backward()
+            b_ms = timed_cold(run_backward, args.steps)
+            for _ in range(args.warmup):
+                run_forward_train()
+                run_backward(0)
+            step_ms = timed_cold(lambda: (run_forward_train(), run_backward(0)), args.steps)
+            ft_ms = timed_cold(run_forward_train, args.steps)
+            bs_ms = timed_cold(lambda: run_backward(0), args.steps)
+            # matrix products per call: the recomputed forward (6 n d I) and
+            # the gradients (dh 2, dW_down 2, dx 4, dW_gate_up 4: 12 n d I)
+            b_flops = 18 * n_rows * d * I
+            backward = {"ms": round(b_ms, 5), "flops_per_call": b_flops,
+                        "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 1),
+                        "mfma_frac": round(b_flops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "pairs_per_s": P / (b_ms * 1e-3),
+                        # training step: 6 n d I (forward) + 12 n d I (gradients), no recompute
+                        "training_step": {"ms": round(step_ms, 5), "forward_train_ms": round(ft_ms, 5),
+                                          "backward_saved_ms": round(bs_ms, 5),
+                                          "tflops": round(18 * n_rows * d * I / (step_ms * 1e-3) / 1e12, 1),
+                                          "pairs_per_s": P / (step_ms * 1e-3)}}
+            del gdx, gwgu, gwd, bws, gout
 
     result = {
         "metric": METRIC,
@@ -456,16 +581,27 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "I": I, "pairs": P,
                    "routed_rows": n_rows, "live_experts": live},
+        "timing": {"headline": f"cold: {args.flush_mb} MiB scratch written before each step, HIP events around "
+                               "moe_forward on its stream (the flush outside the events)",
+                   "cold_min_ms": round(t["cold_min_ms"], 5), "cold_median_ms": round(t["cold_median_ms"], 5),
+                   "wall_ms_per_step_with_flush": round(t["wall_ms_with_flush"], 5),
+                   "warm_ms_per_step": round(t["warm_ms"], 5),
+                   "warm_pairs_per_s": P / (t["warm_ms"] * 1e-3)},
         "roofline": roofline,
         "kernels": kernels,
-        "staged_ms_per_step": staged_ms,
-        "staged_gpu_ms_per_step": gpu_ms,
+        "hbm_targets": {"permute_rows_frac": permute_rows["hbm_frac"] if permute_rows else None,
+                        "combine_frac": kernels["combine"].get("hbm_frac"), "target": 0.70},
+        "staged_gpu_ms_per_step": t["staged_ms"],
         "graph_ms_per_step": graph_ms,
-        "permute_gbs": permute_rows["gbs"],
+        "permute_gbs": permute_rows["gbs"] if permute_rows else None,
         "permute_rows": permute_rows,
         "router_projection": router,
         "backward": backward,
     }
+    extras = [] if args.extra in ("", "none") else [w for w in args.extra.split(",") if w != args.workload]
+    if extras:
+        result["other_workloads"] = {w: measure_extra(lib, tre, torch, w, flush, args.steps, args.warmup)
+                                     for w in extras}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     else:

@@ -47,10 +47,10 @@ BF16 = 1
 _lib = None
 
 
-def build(src: str = SRC_PATH, out: str = LIB_PATH) -> str:
+def build(src: str = SRC_PATH, out: str = LIB_PATH, extra_flags=()) -> str:
     """Compile the oracle's C source into a shared library (gcc, -O2, no
-    fast-math, no FMA contraction)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
+    fast-math, no FMA contraction; ``extra_flags`` for instrumented builds)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off", *extra_flags,
            src, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
@@ -61,9 +61,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    # TRE_ORACLE_LIB: another build of the same source (the sanitizer test
+    # runs the pins against an instrumented copy)
+    path = os.environ.get("TRE_ORACLE_LIB", LIB_PATH)
+    if path == LIB_PATH and not os.path.exists(LIB_PATH):
         build()
-    _lib = _bind(ctypes.CDLL(LIB_PATH))
+    _lib = _bind(ctypes.CDLL(path))
     return _lib
 
 
@@ -93,9 +96,18 @@ def _dtype_code(a: np.ndarray) -> int:
     raise TypeError(f"expected float32 or uint16 (bfloat16 bits), got {a.dtype}")
 
 
+# At most this many threads: on a shared multi-GPU host one GPU's job is
+# given a share of 16 CPUs, whatever the machine's total.
+THREAD_CAP = 16
+
+
 def default_threads() -> int:
-    n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    """The CPUs this process may run on, capped at THREAD_CAP."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, THREAD_CAP))
 
 
 def _f64(a: np.ndarray) -> np.ndarray:

@@ -34,3 +34,37 @@ def rel_l2(got, ref) -> float:
 
 # tolerances of the outputs against the oracle: relative L2 over the compared tensor
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def row_rel_l2(got, ref) -> np.ndarray:
+    """Relative L2 error of every row on its own (rows whose reference is all
+    zero report their absolute norm)."""
+    got = as_f64(np.asarray(got))
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def check_outputs(got, ref, tol, label=""):
+    """Whole-tensor relative L2 within tol AND every row within tol on its
+    own: a single wrong or unwritten row (which adds only about 1/sqrt(rows)
+    to the whole-tensor norm) fails the second test.  Returns (whole, worst
+    row error, index of the worst row)."""
+    whole = rel_l2(got, ref)
+    rows = row_rel_l2(got, ref)
+    worst = int(np.argmax(rows)) if rows.size else -1
+    w = float(rows[worst]) if rows.size else 0.0
+    if label:
+        print(f"  {label}: out rel_l2={whole:.3e}, worst row {worst} rel_l2={w:.3e} over {rows.size} rows",
+              flush=True)
+    assert not np.any(np.isnan(as_f64(np.asarray(got)))), f"{label}: NaN in the output"
+    assert whole <= tol, f"{label}: whole-tensor rel_l2 {whole:.3e} > {tol}"
+    assert w <= tol, f"{label}: row {worst} rel_l2 {w:.3e} > {tol}"
+    return whole, w, worst
+
+
+def workloads_bf16(a) -> np.ndarray:
+    """float64 -> bf16 bit patterns (round to nearest even), for tests of the checks."""
+    import workloads
+    return workloads.bf16_bits(np.asarray(a, dtype=np.float32))

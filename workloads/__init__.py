@@ -32,6 +32,7 @@ from __future__ import annotations
 
 import dataclasses
 import os
+import threading
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -97,12 +98,34 @@ def _normal(seed, tag, part, shape, std=1.0) -> np.ndarray:
 
 
 def _expert_weights(seed: int, tag: int, E: int, shape, dtype: str) -> np.ndarray:
-    """[E, *shape] weights ~ N(0, 0.02), each expert from its own stream."""
+    """[E, *shape] weights ~ N(0, 0.02), each expert from its own stream.
+
+    The values are those of ``_normal`` followed by ``bf16_bits`` (same draws,
+    same rounding); each worker thread reuses its own scratch buffers, so the
+    many-gigabyte workloads do not fault in fresh temporaries per expert."""
     out = np.empty((E,) + tuple(shape), dtype=np.float32 if dtype == "f32" else np.uint16)
+    n = int(np.prod(shape))
+    local = threading.local()
 
     def one(e):
-        w = _normal(seed, tag, e, shape, WEIGHT_STD)
-        out[e] = w if dtype == "f32" else bf16_bits(w)
+        if dtype == "f32":
+            _rng(seed, tag, e).standard_normal(dtype=np.float32, out=out[e])
+            out[e] *= np.float32(WEIGHT_STD)
+            return
+        if getattr(local, "f", None) is None:
+            local.f = np.empty(n, dtype=np.float32)
+            local.t = np.empty(n, dtype=np.uint32)
+        f, t = local.f, local.t
+        _rng(seed, tag, e).standard_normal(dtype=np.float32, out=f)
+        f *= np.float32(WEIGHT_STD)
+        u = f.view(np.uint32)
+        # round to nearest even, as bf16_bits: (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        np.right_shift(u, 16, out=t)
+        np.bitwise_and(t, 1, out=t)
+        t += np.uint32(0x7FFF)
+        u += t
+        np.right_shift(u, 16, out=u)
+        out[e].reshape(-1)[:] = u
 
     with ThreadPoolExecutor(max_workers=_threads()) as ex:
         list(ex.map(one, range(E)))
