@@ -176,6 +176,27 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
                        int32_t* pair_row, void* out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* The layer as moe_forward computes it (same kernels, same results bit for
+ * bit), for callers that cannot allocate memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  There is
+ * no workspace argument: the scratch lives in a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ * until the process ends; its device address is looked up on the first call
+ * on each device (with that device current).  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap on one GPU (concurrent streams, or host
+ * threads) race and give wrong results.  Serialise them.
+ *   arguments as moe_forward, without workspace / workspace_bytes
+ * Errors: as moe_forward; MOE_ERR_WORKSPACE when the layer needs more
+ * scratch than MOE_NOALLOC_SCRATCH_BYTES (moe_forward_workspace_size()
+ * tells how much it needs), with nothing enqueued; MOE_ERR_HIP when the
+ * array's address cannot be looked up.                                      */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                               int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt,
+                               int32_t* topk_idx, float* topk_w, int32_t* expert_offsets, int32_t* row_token,
+                               int32_t* pair_row, void* out, void* stream);
+
 /* ---- the layer's backward pass ----------------------------------------------
  * "Expert parallelism", "Adding an implementation": gradients, the routing
  * weights' included, must reach the rank that holds the tokens; "Combining

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(lib):
         "moe_status_string", "moe_route_topk", "moe_permute_workspace_size", "moe_permute",
         "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
         "moe_forward_workspace_size", "moe_forward", "moe_gate_up_swiglu", "moe_down_proj", "moe_route_project",
-        "moe_backward_workspace_size", "moe_backward", "moe_forward_train"}
+        "moe_backward_workspace_size", "moe_backward", "moe_forward_train", "moe_forward_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -168,3 +168,18 @@ def test_forward_train_validation(lib):
     assert call(out=None) == 1
     assert call(ws_bytes=64) == 3             # needs the backward-sized workspace
     assert call(T=0, x=None, out=None) == 0   # empty batch
+
+
+def test_forward_noalloc_validation(lib):
+    # the layer without a workspace refuses what its static scratch cannot
+    # hold before anything is looked up or enqueued, and validates like
+    # moe_forward
+    f = lib.moe_forward_noalloc
+    cap = tre.noalloc_scratch_bytes()
+    T, d, E, k, I = 8192, 1024, 16, 2, 2048
+    assert lib.moe_forward_workspace_size(T, d, E, k, I, 1) > cap
+    big = [FAKE, FAKE, T, d, E, k, I, FAKE, FAKE, 1, FAKE, FAKE, None, None, None, FAKE, None]
+    assert f(*big) == 3                                              # more than the scratch
+    assert f(*big[:3], 1000, *big[4:]) == 2                          # d % 64
+    assert f(*big[:4], 300, *big[5:]) == 2                           # E > 256
+    assert f(*big[:9], 7, *big[10:]) == 1                            # bad dtype

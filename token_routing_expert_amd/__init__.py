@@ -73,6 +73,7 @@ def load(build_if_missing: bool = True):
         "moe_backward_workspace_size": ([i32, i32, i32, i32, i32, st], sz),
         "moe_backward": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, p, i32, p, sz, p], st),
         "moe_forward_train": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, sz, p], st),
+        "moe_forward_noalloc": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -330,6 +331,43 @@ def moe_forward(x, w_gate_up, w_down, k: int, logits=None, topk_idx=None, topk_w
     _check("moe_forward", lib.moe_forward(_ptr(x), _ptr(logits), T, d, E, k, I, _ptr(w_gate_up), _ptr(w_down), dt,
                                           _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token),
                                           _ptr(pair_row), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out, topk_idx, topk_w
+
+
+def noalloc_scratch_bytes() -> int:
+    """MOE_NOALLOC_SCRATCH_BYTES of include/moe.h: the scratch moe_forward_noalloc has."""
+    m = re.search(r"#define\s+MOE_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER_PATH).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+def moe_forward_noalloc(x, w_gate_up, w_down, k: int, out, topk_idx, topk_w, logits=None, expert_offsets=None,
+                        row_token=None, pair_row=None, stream=None):
+    """The whole layer as moe_forward computes it, with the library's static
+    scratch instead of a workspace: nothing is allocated, so every output
+    (out [T, d], topk_idx / topk_w [T, k]) must be given.  Calls that overlap
+    on one GPU race.  Returns (out, topk_idx, topk_w)."""
+    torch = _torch()
+    lib = load()
+    T, d = x.shape
+    E, d2, two_i = w_gate_up.shape
+    I = two_i // 2
+    if d2 != d or two_i != 2 * I:
+        raise ValueError(f"w_gate_up {tuple(w_gate_up.shape)} does not match d={d}")
+    _expect(w_gate_up, x.dtype, (E, d, 2 * I), "w_gate_up")
+    _expect(w_down, x.dtype, (E, I, d), "w_down")
+    if logits is not None:
+        _expect(logits, torch.float32, (T, E), "logits")
+    _expect(topk_idx.reshape(T, k), torch.int32, (T, k), "topk_idx")
+    _expect(topk_w.reshape(T, k), torch.float32, (T, k), "topk_w")
+    _expect(out, x.dtype, (T, d), "out")
+    for name, t, n in (("expert_offsets", expert_offsets, E + 1), ("row_token", row_token, T * k),
+                       ("pair_row", pair_row, T * k)):
+        if t is not None:
+            _expect(t, torch.int32, (n,), name)
+    _check("moe_forward_noalloc",
+           lib.moe_forward_noalloc(_ptr(x), _ptr(logits), T, d, E, k, I, _ptr(w_gate_up), _ptr(w_down), _dt(x),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token),
+                                   _ptr(pair_row), _ptr(out), _stream(stream)))
     return out, topk_idx, topk_w
 
 

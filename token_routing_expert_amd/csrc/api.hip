@@ -4,6 +4,8 @@
 #include "../../include/moe.h"
 #include "common.hpp"
 
+#include <mutex>
+
 using namespace tre;
 
 namespace {
@@ -256,10 +258,14 @@ size_t moe_forward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, in
   return forward_layout(T, d, E, k, I, dt).total;
 }
 
-moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
-                       const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
-                       int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row, void* out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer's arguments, workspace aside (T == 0 is valid: nothing to do).
+moe_status check_forward_args(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                              int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt,
+                              const int32_t* topk_idx, const float* topk_w, const void* out) {
   if (!dtype_ok(dt) || T < 0 || k < 1) return MOE_ERR_ARG;
   TRY(check_experts(E));
   if (logits && k > E) return MOE_ERR_ARG;
@@ -272,6 +278,17 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
   if ((int64_t)T * d >= kMaxElems / 2) return MOE_ERR_UNSUPPORTED;   // x is addressed with 32-bit byte offsets
   if (T == 0) return MOE_OK;
   if (!x || !w_gate_up || !w_down || !topk_idx || !topk_w || !out) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+// The layer (moe_forward's work) with its scratch in `workspace`.
+moe_status forward_impl(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
+                        const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
+                        int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  TRY(check_forward_args(x, logits, T, d, E, k, I, w_gate_up, w_down, dt, topk_idx, topk_w, out));
+  if (T == 0) return MOE_OK;
+  const int64_t P = (int64_t)T * k;
   const ForwardLayout L = forward_layout(T, d, E, k, I, dt);
   if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
 
@@ -312,6 +329,66 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
   TRY(from_hip(launch_grouped_ffn_f32((const float*)x_perm, offs, P, E, d, I, (const float*)w_gate_up,
                                       (const float*)w_down, (float*)h, (float*)y_perm, s)));
   return from_hip(launch_combine_f32((const float*)y_perm, P, p_row, topk_w, T, k, d, (float*)out, s));
+}
+
+// ---- the layer without a workspace: scratch in a static device array ----
+//
+// Every GPU the library runs on holds its own copy of `scratch` (at its own
+// address) until the process ends.  Host code never passes the array's name
+// to a kernel or a copy (on the host it is only a stand-in for the symbol):
+// the device address is looked up once per device with hipGetSymbolAddress,
+// with that device current, and kept.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on its first use on
+// that device.
+hipError_t scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
+                       const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return forward_impl(x, logits, T, d, E, k, I, w_gate_up, w_down, dt, topk_idx, topk_w, expert_offsets, row_token,
+                      pair_row, out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_forward_noalloc(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                               int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx,
+                               float* topk_w, int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row,
+                               void* out, void* stream) {
+  // the arguments first, then the size: a layer that needs more scratch
+  // than the array holds is refused before anything is looked up or enqueued
+  TRY(check_forward_args(x, logits, T, d, E, k, I, w_gate_up, w_down, dt, topk_idx, topk_w, out));
+  if (T == 0) return MOE_OK;
+  if (forward_layout(T, d, E, k, I, dt).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return forward_impl(x, logits, T, d, E, k, I, w_gate_up, w_down, dt, topk_idx, topk_w, expert_offsets, row_token,
+                      pair_row, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t moe_backward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, moe_dtype dt) {
