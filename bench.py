@@ -8,9 +8,10 @@ SwiGLU, reading the token rows in place -> down projection -> combine: the
 kernels the fused entry point moe_forward launches.
 
 Timing is HBM-honest: before every timed step a scratch buffer larger than
-the 256 MB Infinity Cache (512 MiB by default) is written on the same stream,
+the 256 MB Infinity Cache (512 MiB by default) is read on the same stream,
 so no operand of the step is served from a cache left warm by the step
-before; HIP events on the stream bracket the step itself (not the flush).
+before (a read, so that no dirty lines are left for the step to write
+back); HIP events on the stream bracket the step itself (not the flush).
 The headline (value, ms_per_step) is K such steps through moe_forward; the
 same K steps run again as separate C-ABI calls with events between the
 stages, which gives every kernel's average duration; a warm figure (steps
@@ -239,17 +240,21 @@ class Layer:
 
 
 class Flush:
-    """Writes a scratch buffer larger than the Infinity Cache on the stream,
-    so that the next step reads its operands from HBM."""
+    """Reads a scratch buffer larger than the Infinity Cache on the stream, so
+    that the next step finds none of its operands in L2 or the Infinity Cache
+    and reads them from HBM.  A read, not a write: a written buffer would
+    leave the caches full of dirty lines whose write-back the next step would
+    pay for."""
 
     def __init__(self, torch, mib: int):
-        self.buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda") if mib > 0 else None
-        self.v = 0
+        self.buf = None
+        if mib > 0:
+            self.buf = torch.zeros((mib << 20) // 4, dtype=torch.float32, device="cuda")
+            torch.cuda.synchronize()
 
     def __call__(self):
         if self.buf is not None:
-            self.v = (self.v + 1) & 0xFF
-            self.buf.fill_(self.v)
+            self.buf.sum()
 
 
 def time_layer(torch, layer, flush, steps: int, warmup: int):
@@ -378,7 +383,7 @@ def main() -> int:
                     help="comma-separated workloads measured beside the headline (cold layer and kernels), "
                          "or 'none'")
     ap.add_argument("--flush-mb", type=int, default=512,
-                    help="MiB of scratch written before every timed step (0: no flush)")
+                    help="MiB of scratch read before every timed step (0: no flush)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the router projection, permute-with-rows, graph and backward measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -581,7 +586,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "I": I, "pairs": P,
                    "routed_rows": n_rows, "live_experts": live},
-        "timing": {"headline": f"cold: {args.flush_mb} MiB scratch written before each step, HIP events around "
+        "timing": {"headline": f"cold: {args.flush_mb} MiB scratch read before each step, HIP events around "
                                "moe_forward on its stream (the flush outside the events)",
                    "cold_min_ms": round(t["cold_min_ms"], 5), "cold_median_ms": round(t["cold_median_ms"], 5),
                    "wall_ms_per_step_with_flush": round(t["wall_ms_with_flush"], 5),
