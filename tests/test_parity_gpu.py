@@ -271,6 +271,20 @@ def test_grouped_ffn_random(tre, T, d, E, k, I, dtype):
     check_grouped_ffn(tre, inp, idx)
 
 
+@pytest.mark.parametrize("counts", [(257, 288, 289, 300, 250), (288, 288, 288, 33, 0, 512, 544)])
+def test_grouped_ffn_tall_tiles(tre, counts):
+    # Experts of 257-288 rows: the down projection's last 256-row tile then
+    # also takes the expert's last 1-32 rows (a tall tile) instead of a tile
+    # of its own; 289 rows and more keep a separate tile.  Every grouped row
+    # against the oracle (and none past the routed rows written).
+    counts = np.array(counts)
+    E, T = len(counts), int(counts.sum())
+    inp = workloads.make_custom(T=T, d=256, E=E, k=1, I=320, dtype="bf16", seed=T, logits="normal")
+    idx = np.random.default_rng(T).permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(T, 1)
+    say(f"grouped ffn tall tiles, counts {counts.tolist()}")
+    check_grouped_ffn(tre, inp, idx)
+
+
 def test_grouped_ffn_empty_experts(tre):
     inp = workloads.make_custom(T=200, d=128, E=16, k=2, I=128, dtype="bf16", seed=5, logits="normal")
     idx = np.where(np.arange(400).reshape(200, 2) % 2 == 0, 3, 11).astype(np.int32)   # only experts 3, 11

@@ -163,7 +163,7 @@ struct Tile {
 // tile never waits on a plain global load (which would drain the ring).
 // (launch bounds: workgroup size and waves per SIMD -- OCC workgroups of
 // 2 WM waves per CU need OCC WM / 2 of them, at least one)
-template <int EPI, bool BT, int BK, int OCC, int NJ, int WM, int NS, bool PP>
+template <int EPI, bool BT, int BK, int OCC, int NJ, int WM, int NS, bool PP, bool TL>
 __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K, int N, int ldw,
     const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles, const int32_t* __restrict__ row_token,
@@ -188,7 +188,18 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   constexpr bool SCATTER = EPI == kEpiScatter;
   static_assert(!SCATTER || WAVES >= 2, "the row weights are fetched by wave 1");
   constexpr int NSLOT = SCATTER ? 4 : 2;
-  __shared__ __attribute__((aligned(1024))) char sA[NS * GE::A_BYTES];
+  // Tall tiles (TL: the ping-pong plain product over already grouped rows):
+  // an expert's last tile also takes up to XR = 32 rows past BM, so that they
+  // do not make a tile of their own -- one that would stream the expert's
+  // whole weight slice again, and run its whole stage loop, for a few rows.
+  // Waves 0 and 1 load the extra 32-row block with one more load each per
+  // stage; each wave multiplies it with one of its own column blocks (the
+  // wm-th), so the block costs one MFMA per wave and k-step.
+  constexpr bool TALL = TL;
+  static_assert(!TL || (PP && EPI == kEpiPlain && !BT), "tall tiles: ping-pong plain products only");
+  constexpr int XR = TALL ? 32 : 0;
+  constexpr int A_STAGE = GE::A_BYTES + XR * BK * 2;  // LDS bytes of an activation stage
+  __shared__ __attribute__((aligned(1024))) char sA[NS * A_STAGE];
   __shared__ __attribute__((aligned(1024))) char sB[NS * GE::B_BYTES];
   __shared__ __attribute__((aligned(1024))) int32_t s_rt[NSLOT][256];
   __shared__ __attribute__((aligned(1024))) float s_rw[SCATTER ? NSLOT : 1][256];
@@ -213,6 +224,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     s_lo[tid] = lo;
     s_cnt[tid] = hi - lo;
     mt = (int)ceil_div(hi - lo, BM);
+    if (TALL && mt > 1 && (hi - lo) - (mt - 1) * BM <= XR) mt -= 1;  // the last tile takes the rest
     s_mt[tid] = mt;
   }
   int total_mt = 0;
@@ -279,7 +291,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     Tile t;
     t.e = e;
     t.row0 = (int64_t)e_lo + (int64_t)mtile * BM;
-    t.rows = min(BM, e_cnt - mtile * BM);
+    t.rows = (TALL && mtile == e_mt - 1) ? e_cnt - mtile * BM : min(BM, e_cnt - mtile * BM);
     t.n0 = (int)nt * BNO;
     return t;
   };
@@ -336,6 +348,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferConfig);
   __amdgpu_buffer_rsrc_t b_rsrc = a_rsrc;
   uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
+  uint32_t ax_voff = kOutOfRange;  // tall tiles: this lane's chunk of the extra rows (waves 0, 1)
   // byte offsets of the next stage's k-columns in the activation and weight
   // buffers: scalar, added to every lane's offset by the load itself
   uint32_t ka = 0, kb = 0;
@@ -394,6 +407,12 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
                       ? (uint32_t)(src * K + c * 8) * 2u
                       : kOutOfRange;
     }
+    if constexpr (TALL) {
+      // rows BM + 16 wave .. + 15 of the tile, the A buffer spans t.rows rows
+      const int r = BM + 16 * wave + lane / GE::CPR;
+      const int c = (lane % GE::CPR) ^ GE::swz(r);
+      ax_voff = (wave < 2 && r < t.rows) ? (uint32_t)(r * K + c * 8) * 2u : kOutOfRange;
+    }
 #pragma unroll
     for (int p = 0; p < GE::B_INSTR; ++p) {
       if constexpr (BT) {
@@ -442,7 +461,11 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     if (i_k == 0) enter();
 #pragma unroll
     for (int p = 0; p < GE::A_INSTR; ++p)
-      dma16s(a_rsrc, a_lds0 + SLOT * GE::A_BYTES + p * WAVES * 1024, a_voff[p], ka);
+      dma16s(a_rsrc, a_lds0 + SLOT * A_STAGE + p * WAVES * 1024, a_voff[p], ka);
+    // in every stage, tall tile or not, so that waves 0 and 1 always count
+    // exactly one load more per stage (past the tile's rows it fetches nothing)
+    if constexpr (TALL)
+      if (wave < 2) dma16s(a_rsrc, a_lds0 + SLOT * A_STAGE + GE::A_BYTES, ax_voff, ka);
 #pragma unroll
     for (int p = 0; p < GE::B_INSTR; ++p)
       dma16s(b_rsrc, b_lds0 + SLOT * GE::B_BYTES + p * WAVES * 1024, b_voff[p], kb);
@@ -456,7 +479,13 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
 
   // ---- compute side ----
   f32x16 acc[NJ][2];
+  f32x16 acc_x;           // tall tiles: rows BM .. BM + 31, column block col_base(wm)
+  bool cur_tall = false;  // the tile being multiplied has rows past BM
   auto zero_acc = [&]() {
+    if constexpr (TALL) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc_x[q] = 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -467,6 +496,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
 
   struct Frag {
     bf16x8 a[2], b[NJ];
+    bf16x8 ax;  // tall tiles: the extra rows
   };
   auto read_frag = [&](const char* a_buf, const char* b_buf, int ks, Frag& f) {
 #pragma unroll
@@ -485,6 +515,9 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       const uint32_t off = GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
       f.b[j] = lds_read_b_operand((const bf16_t*)(b_buf + off), (const bf16_t*)(b_buf + off + 4 * GE::BROW));
     }
+    if constexpr (TALL) {
+      if (cur_tall) f.ax = *(const bf16x8*)(a_buf + GE::a_byte(BM + lane % 32, ks * 2 + lane / 32));
+    }
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
@@ -492,6 +525,16 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
+    if constexpr (TALL) {
+      if (cur_tall) {
+        // the wm-th column block, selected without indexing the fragments at
+        // run time (which would put them in scratch memory)
+        bf16x8 bw = f.b[0];
+#pragma unroll
+        for (int j = 1; j < NJ; ++j) bw = wm == j ? f.b[j] : bw;
+        acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, f.ax, acc_x, 0, 0, 0);
+      }
+    }
   };
 
   // acc[j][i] holds output row 64 wm + 32 i + lane % 32, columns
@@ -622,6 +665,22 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
           }
       }
     }
+    if constexpr (TALL) {
+      // the extra rows: acc_x holds row BM + lane % 32, the wave's wm-th
+      // column block
+      const int r = BM + lr;
+      if (t.rows > BM && r < t.rows) {
+        bf16_t* orow = Out + (t.row0 + r) * N;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c = t.n0 + WCOL * wn + 32 * wm + 8 * q4 + lc;
+          if (c >= N) continue;
+          const uint32_t p0 = pack_bf16x2(acc_x[4 * q4], acc_x[4 * q4 + 1]);
+          const uint32_t p1 = pack_bf16x2(acc_x[4 * q4 + 2], acc_x[4 * q4 + 3]);
+          *(uint2*)(orow + c) = make_uint2(p0, p1);
+        }
+      }
+    }
   };
 
   // ---- the stage stream ----
@@ -661,7 +720,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   auto stage = [&](auto slot_c, bool active, int& left) {
     constexpr int SLOT = decltype(slot_c)::value;
     constexpr int ISSUE = (SLOT + NS - 1) % NS;  // the slot stage g + NS - 1 lands in
-    const char* a_buf = sA + SLOT * GE::A_BYTES;
+    const char* a_buf = sA + SLOT * A_STAGE;
     const char* b_buf = sB + SLOT * GE::B_BYTES;
     const bool more = g + NS - 1 < total;
     if constexpr (!PP) {
@@ -702,8 +761,13 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
         read_frag(a_buf, b_buf, 0, f0);
         read_frag(a_buf, b_buf, 1, f1);
       }
-      if (more) wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
-      else wait_vmcnt<0>();
+      if (more) {
+        // (tall tiles: waves 0 and 1 issue one load more per stage)
+        if (TALL && wave < 2) wait_vmcnt<(NS - 2) * (GE::PER_STAGE + 1)>();
+        else wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
+      } else {
+        wait_vmcnt<0>();
+      }
       if (post_cnt > 0 && --post_cnt == 0) post();
       wait_lgkm0();
       barrier();
@@ -733,6 +797,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     // the slice's stages in L2 (measured: the projection 1.4-4.4% faster).
     constexpr bool kKeepPace = PP && (EPI == kEpiPlain || EPI == kEpiScatter);
     const bool active = kKeepPace || 64 * wm < cur.rows;
+    cur_tall = TALL && cur.rows > BM;
     int left = k_begin(cur_split + 1) - k_begin(cur_split);
     // the unrolled ring, entered at the slot of the tile's first stage: the
     // copies before it are skipped in the first round only (one entry, so
@@ -835,7 +900,8 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float* __restrict__ 
   y[r * d + c] = acc;
 }
 
-template <int EPI, bool BT = false, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2, int NS = 3, bool PP = false>
+template <int EPI, bool BT = false, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2, int NS = 3, bool PP = false,
+          bool TL = false>
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
                       int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr, int n_split = 1,
@@ -844,7 +910,7 @@ hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows,
   constexpr int BNO = SWIGLU ? 32 * NJ : 64 * NJ;   // output columns per tile
   if (K / BK / n_split < NS - 1) return hipErrorInvalidValue;  // each range spans at least NS - 1 stages
   const int nt = (int)ceil_div(N, BNO);
-  dma::k_grouped_gemm<EPI, BT, BK, OCC, NJ, WM, NS, PP>
+  dma::k_grouped_gemm<EPI, BT, BK, OCC, NJ, WM, NS, PP, TL>
       <<<persistent_grid(max_rows, E, 64 * WM, nt * n_split, OCC), 128 * WM, 0, s>>>(
           a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows, out2, aux, n_split, part, sched, row_w);
   return hipGetLastError();
@@ -928,10 +994,23 @@ bool big_tiles(int64_t max_rows, int E, int K) { return max_rows >= 128 * (int64
 // The tile list is set up with one thread per expert, so E <= 128.
 bool small_tiles(int64_t max_rows, int E) { return max_rows <= 64 * (int64_t)E && E <= 128; }
 
+// Tall 256-row tiles for the plain products (the down projection) when the
+// experts hold at most 384 rows on average: an expert then has one or two
+// tiles, and a second tile of a few rows would cost about half a full one
+// (measured on the 128-expert layer: down 881 -> 743 us).  With more rows per
+// expert such tails are rare and the always-issued extra load costs more
+// than it saves (down 74 -> 86 us at 512 rows per expert).
+bool tall_tiles(int64_t max_rows, int E) { return max_rows <= 384 * (int64_t)E; }
+
 template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token, int64_t a_rows,
                        bf16_t* out2, const bf16_t* aux, int32_t* sched) {
+  if constexpr (EPI == kEpiPlain && !BT) {
+    if (big_tiles(max_rows, E, K) && tall_tiles(max_rows, E) && row_token == nullptr)
+      return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, nullptr,
+                                                             0, out2, aux, 1, nullptr, sched);
+  }
   if (big_tiles(max_rows, E, K))
     return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
                                                      a_rows, out2, aux, 1, nullptr, sched);
