@@ -273,10 +273,10 @@ def test_grouped_ffn_random(tre, T, d, E, k, I, dtype):
 
 @pytest.mark.parametrize("counts", [(257, 288, 289, 300, 250), (288, 288, 288, 33, 0, 512, 544)])
 def test_grouped_ffn_tall_tiles(tre, counts):
-    # Experts of 257-288 rows: the down projection's last 256-row tile then
-    # also takes the expert's last 1-32 rows (a tall tile) instead of a tile
-    # of its own; 289 rows and more keep a separate tile.  Every grouped row
-    # against the oracle (and none past the routed rows written).
+    # Experts of 257-288 rows: the gate/up and down projections' last 256-row
+    # tile then also takes the expert's last 1-32 rows (a tall tile) instead
+    # of a tile of its own; 289 rows and more keep a separate tile.  Every
+    # grouped row against the oracle (and none past the routed rows written).
     counts = np.array(counts)
     E, T = len(counts), int(counts.sum())
     inp = workloads.make_custom(T=T, d=256, E=E, k=1, I=320, dtype="bf16", seed=T, logits="normal")
@@ -295,9 +295,29 @@ def test_grouped_ffn_empty_experts(tre):
 def test_gate_up_reads_token_rows_in_place(tre, T, d, E, k, I):
     # index-only permutation + the projection reading x[row_token[r]] gives the
     # same h, bit for bit, as moving the rows first
-    torch = _torch()
     inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + 1, logits="normal_bias")
     idx, _ = oracle.route(inp.logits, k)
+    check_gate_up_in_place(tre, inp, idx)
+
+
+@pytest.mark.parametrize("counts", [(257, 288, 289, 300, 250), (288, 33, 0, 270, 512)])
+def test_gate_up_tall_tiles_in_place(tre, counts):
+    # Experts of 257-288 rows: the gate/up projection's last 256-row tile also
+    # takes the expert's last 1-32 rows, whose token indices arrive by a second
+    # index load; reading token rows in place must still give h bit for bit as
+    # from moved rows, and the rows must match the oracle
+    counts = np.array(counts)
+    E, T = len(counts), int(counts.sum())
+    inp = workloads.make_custom(T=T, d=256, E=E, k=1, I=320, dtype="bf16", seed=T + 7, logits="normal")
+    idx = np.random.default_rng(T + 7).permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(T, 1)
+    say(f"gate/up tall tiles reading token rows, counts {counts.tolist()}")
+    check_gate_up_in_place(tre, inp, idx)
+
+
+def check_gate_up_in_place(tre, inp, idx):
+    torch = _torch()
+    T, d, E, I = inp.T, inp.d, inp.E, inp.I
+    k = idx.shape[1]
     xd, pe = to_device(inp.x), to_device(idx.reshape(-1))
     wgu = to_device(inp.w_gate_up)
     x_perm, row_token, pair_row, offsets = tre.moe_permute(xd, pe, k, E)

@@ -188,20 +188,27 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   constexpr bool SCATTER = EPI == kEpiScatter;
   static_assert(!SCATTER || WAVES >= 2, "the row weights are fetched by wave 1");
   constexpr int NSLOT = SCATTER ? 4 : 2;
-  // Tall tiles (TL: the ping-pong plain product over already grouped rows):
-  // an expert's last tile also takes up to XR = 32 rows past BM, so that they
-  // do not make a tile of their own -- one that would stream the expert's
-  // whole weight slice again, and run its whole stage loop, for a few rows.
-  // Waves 0 and 1 load the extra 32-row block with one more load each per
-  // stage; each wave multiplies it with one of its own column blocks (the
-  // wm-th), so the block costs one MFMA per wave and k-step.
+  // Tall tiles (TL: the ping-pong plain and gate/up products): an expert's
+  // last tile also takes up to XR = 32 rows past BM, so that they do not make
+  // a tile of their own -- one that would stream the expert's whole weight
+  // slice again, and run its whole stage loop, for a few rows.  Waves 0 and 1
+  // load the extra 32-row block with one more load each per stage (with
+  // row_token, its token indices arrive with the tile's by a second index
+  // load).  Each wave multiplies the block with 32 weight columns: its wm-th
+  // column block in the plain product; in the gate/up product, 16 of its gate
+  // columns and the 16 matching up columns, read as one fragment, so that
+  // SwiGLU pairs stay in one lane.  The block costs one MFMA per wave and
+  // k-step.
   constexpr bool TALL = TL;
-  static_assert(!TL || (PP && EPI == kEpiPlain && !BT), "tall tiles: ping-pong plain products only");
+  static_assert(!TL || (PP && (EPI == kEpiPlain || EPI == kEpiSwiglu) && !BT),
+                "tall tiles: ping-pong plain or gate/up products only");
   constexpr int XR = TALL ? 32 : 0;
   constexpr int A_STAGE = GE::A_BYTES + XR * BK * 2;  // LDS bytes of an activation stage
   __shared__ __attribute__((aligned(1024))) char sA[NS * A_STAGE];
   __shared__ __attribute__((aligned(1024))) char sB[NS * GE::B_BYTES];
-  __shared__ __attribute__((aligned(1024))) int32_t s_rt[NSLOT][256];
+  // (tall tiles: the index of rows BM .. BM + XR - 1 arrives by a second
+  // 1 KB load, so a slot spans 512 entries)
+  __shared__ __attribute__((aligned(1024))) int32_t s_rt[NSLOT][TALL ? 512 : 256];
   __shared__ __attribute__((aligned(1024))) float s_rw[SCATTER ? NSLOT : 1][256];
   __shared__ int s_start[kMaxExperts];
   __shared__ int s_mt[kMaxExperts];
@@ -368,6 +375,13 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(row_token + t.row0), (short)0, bytes, kBufferConfig);
       dma16(rs, __builtin_amdgcn_readfirstlane(lds_address(&s_rt[slot][0])), (uint32_t)lane * 16u);
+      if constexpr (TALL) {
+        // rows 256 .. of a tall tile (none: every lane reads past the buffer)
+        const int xbytes = __builtin_amdgcn_readfirstlane(max(t.rows - 256, 0) * 4);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(row_token + t.row0 + min(t.rows, 256)), (short)0, xbytes, kBufferConfig);
+        dma16(rx, __builtin_amdgcn_readfirstlane(lds_address(&s_rt[slot][256])), (uint32_t)lane * 16u);
+      }
     }
     if constexpr (SCATTER) {
       if (wave == 1) {
@@ -411,7 +425,11 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       // rows BM + 16 wave .. + 15 of the tile, the A buffer spans t.rows rows
       const int r = BM + 16 * wave + lane / GE::CPR;
       const int c = (lane % GE::CPR) ^ GE::swz(r);
-      ax_voff = (wave < 2 && r < t.rows) ? (uint32_t)(r * K + c * 8) * 2u : kOutOfRange;
+      int64_t src = r;
+      if (gather) src = (wave < 2 && r < t.rows) ? s_rt[slot][r] : -1;
+      ax_voff = (wave < 2 && r < t.rows && src >= 0 && src < (gather ? a_rows : (int64_t)t.rows))
+                    ? (uint32_t)(src * K + c * 8) * 2u
+                    : kOutOfRange;
     }
 #pragma unroll
     for (int p = 0; p < GE::B_INSTR; ++p) {
@@ -479,7 +497,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
 
   // ---- compute side ----
   f32x16 acc[NJ][2];
-  f32x16 acc_x;           // tall tiles: rows BM .. BM + 31, column block col_base(wm)
+  f32x16 acc_x;           // tall tiles: rows BM .. BM + 31 times the wave's extra columns
   bool cur_tall = false;  // the tile being multiplied has rows past BM
   auto zero_acc = [&]() {
     if constexpr (TALL) {
@@ -497,26 +515,73 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   struct Frag {
     bf16x8 a[2], b[NJ];
     bf16x8 ax;  // tall tiles: the extra rows
+    bf16x8 bx;  // tall gate/up tiles: 16 gate columns and their 16 up columns
   };
-  auto read_frag = [&](const char* a_buf, const char* b_buf, int ks, Frag& f) {
+  // Per-lane LDS addresses of this wave's fragment reads in ring slot 0 at
+  // k-step 0.  Every read of the stage loop sits a constant offset from one
+  // of them (ring slot, k-step, 32-row block, and for gate/up the up half of
+  // the columns), which the read takes as its immediate offset.  The XOR
+  // swizzles hide that linearity from the compiler, which otherwise keeps a
+  // register or two per read; the empty asm statements make each base an
+  // opaque value, computed once.
+  constexpr int NFB = SWIGLU ? NJ / 2 : NJ;  // distinct weight-read bases (BT: none, see read_frag)
+  uint32_t fa[2], fb[NFB], fax[2] = {0u, 0u}, fbx = 0u;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 64 * wm + 32 * i + lane % 32;
-      f.a[i] = *(const bf16x8*)(a_buf + GE::a_byte(r, ks * 2 + lane / 32));
+  for (int ks = 0; ks < 2; ++ks) {
+    fa[ks] = lds_address(sA) + GE::a_byte(64 * wm + lane % 32, ks * 2 + lane / 32);
+    asm("" : "+v"(fa[ks]));
+    if constexpr (TALL) {
+      fax[ks] = lds_address(sA) + GE::a_byte(BM + lane % 32, ks * 2 + lane / 32);
+      asm("" : "+v"(fax[ks]));
     }
+  }
+#pragma unroll
+  for (int j = 0; j < NFB; ++j) {
+    if constexpr (!BT) {
+      const int kr = (g16 / 2) * 8 + L / 4;
+      const int col = col_base(j) + (g16 % 2) * 16 + 4 * (L % 4);
+      fb[j] = lds_address(sB) + GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
+      asm("" : "+v"(fb[j]));
+    }
+  }
+  if constexpr (TALL && SWIGLU) {
+    // the wave's 16 gate columns (WCOL / 2) wn + 16 wm + 0..15 in the extra
+    // fragment's first 16 columns, their up columns in its last 16
+    const int kr = (g16 / 2) * 8 + L / 4;
+    const int col = (WCOL / 2) * wn + 16 * wm + (g16 % 2) * (BNB / 2) + 4 * (L % 4);
+    fbx = lds_address(sB) + GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
+    asm("" : "+v"(fbx));
+  }
+  typedef __attribute__((address_space(3))) const char lds_char;
+  auto lds_at = [](uint32_t a) { return (lds_char*)(uintptr_t)a; };
+  auto read_a = [&](uint32_t base, int off) { return *(const __attribute__((address_space(3))) bf16x8*)(lds_at(base) + off); };
+  auto read_b = [&](uint32_t base, int off) {
+    lds_char* p = lds_at(base) + off;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * GE::BROW));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // the stage in ring slot SLOT, k-step ks
+  auto read_frag = [&](auto slot_c, int ks, Frag& f) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    constexpr int A_OFF = SLOT * A_STAGE, B_OFF = SLOT * GE::B_BYTES;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = read_a(fa[ks], A_OFF + i * 32 * BK * 2);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if constexpr (BT) {
-        f.b[j] = *(const bf16x8*)(b_buf + GE::a_byte(col_base(j) + lane % 32, ks * 2 + lane / 32));
+        // weight rows held like activation rows (the backward's products)
+        f.b[j] = *(const bf16x8*)(sB + B_OFF + GE::a_byte(col_base(j) + lane % 32, ks * 2 + lane / 32));
         continue;
       }
-      const int kr = ks * 16 + (g16 / 2) * 8 + L / 4;
-      const int col = col_base(j) + (g16 % 2) * 16 + 4 * (L % 4);
-      const uint32_t off = GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
-      f.b[j] = lds_read_b_operand((const bf16_t*)(b_buf + off), (const bf16_t*)(b_buf + off + 4 * GE::BROW));
+      const bool up = SWIGLU && j >= NJ / 2;  // the up half: BNB / 2 columns = BNB bytes on
+      f.b[j] = read_b(fb[up ? j - NJ / 2 : j], B_OFF + ks * 16 * GE::BROW + (up ? BNB : 0));
     }
     if constexpr (TALL) {
-      if (cur_tall) f.ax = *(const bf16x8*)(a_buf + GE::a_byte(BM + lane % 32, ks * 2 + lane / 32));
+      if (cur_tall) {
+        f.ax = read_a(fax[ks], A_OFF);
+        if constexpr (SWIGLU) f.bx = read_b(fbx, B_OFF + ks * 16 * GE::BROW);
+      }
     }
   };
   auto mma = [&](const Frag& f) {
@@ -527,12 +592,16 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
     if constexpr (TALL) {
       if (cur_tall) {
-        // the wm-th column block, selected without indexing the fragments at
-        // run time (which would put them in scratch memory)
-        bf16x8 bw = f.b[0];
+        if constexpr (SWIGLU) {
+          acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.bx, f.ax, acc_x, 0, 0, 0);
+        } else {
+          // the wm-th column block, selected without indexing the fragments
+          // at run time (which would put them in scratch memory)
+          bf16x8 bw = f.b[0];
 #pragma unroll
-        for (int j = 1; j < NJ; ++j) bw = wm == j ? f.b[j] : bw;
-        acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, f.ax, acc_x, 0, 0, 0);
+          for (int j = 1; j < NJ; ++j) bw = wm == j ? f.b[j] : bw;
+          acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, f.ax, acc_x, 0, 0, 0);
+        }
       }
     }
   };
@@ -540,7 +609,12 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   // acc[j][i] holds output row 64 wm + 32 i + lane % 32, columns
   // col_base(j) + 8 q4 + 4 (lane / 32) + {0..3}
   auto epilogue = [&](const Tile& t, int split, int slot) {
-    const int lr = lane % 32, lc = 4 * (lane / 32);
+    // (the lane index is re-read here, through a volatile asm, so that the
+    // compiler does not hoist the epilogue's per-lane column offsets out of
+    // the tile loop and hold them in registers across every stage)
+    int elane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(elane));
+    const int lr = elane % 32, lc = 4 * (elane / 32);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 64 * wm + 32 * i + lr;
@@ -669,7 +743,28 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       // the extra rows: acc_x holds row BM + lane % 32, the wave's wm-th
       // column block
       const int r = BM + lr;
-      if (t.rows > BM && r < t.rows) {
+      if (SWIGLU && t.rows > BM && r < t.rows) {
+        // acc_x[4 q4 + v] is gate column (WCOL / 2) wn + 16 wm + 8 q4 + lc + v
+        // for q4 < 2 and the matching up column for q4 + 2
+        bf16_t* orow = Out + (t.row0 + r) * N;
+#pragma unroll
+        for (int q4 = 0; q4 < 2; ++q4) {
+          const int c = t.n0 + (WCOL / 2) * wn + 16 * wm + 8 * q4 + lc;
+          if (c >= N) continue;
+          uint32_t packed[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float hv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const float gt = acc_x[4 * q4 + 2 * h2 + u], up = acc_x[4 * (q4 + 2) + 2 * h2 + u];
+              hv[u] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
+            }
+            packed[h2] = pack_bf16x2(hv[0], hv[1]);
+          }
+          *(uint2*)(orow + c) = make_uint2(packed[0], packed[1]);
+        }
+      } else if (!SWIGLU && t.rows > BM && r < t.rows) {
         bf16_t* orow = Out + (t.row0 + r) * N;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -720,8 +815,6 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   auto stage = [&](auto slot_c, bool active, int& left) {
     constexpr int SLOT = decltype(slot_c)::value;
     constexpr int ISSUE = (SLOT + NS - 1) % NS;  // the slot stage g + NS - 1 lands in
-    const char* a_buf = sA + SLOT * A_STAGE;
-    const char* b_buf = sB + SLOT * GE::B_BYTES;
     const bool more = g + NS - 1 < total;
     if constexpr (!PP) {
       // this wave's loads of stage g are done (NS - 2 later stages may still
@@ -736,8 +829,8 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       // MFMAs.  A wave whose 64 rows are all past the tile's rows has nothing
       // to multiply.
       if (active) {
-        read_frag(a_buf, b_buf, 0, f0);
-        read_frag(a_buf, b_buf, 1, f1);
+        read_frag(slot_c, 0, f0);
+        read_frag(slot_c, 1, f1);
         __builtin_amdgcn_sched_barrier(0);
         mma(f0);
         mma(f1);
@@ -758,8 +851,8 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       // multiply: its SIMD then serves the other group alone (tiles of an
       // expert's last rows run up to twice as fast)
       if (active) {
-        read_frag(a_buf, b_buf, 0, f0);
-        read_frag(a_buf, b_buf, 1, f1);
+        read_frag(slot_c, 0, f0);
+        read_frag(slot_c, 1, f1);
       }
       if (more) {
         // (tall tiles: waves 0 and 1 issue one load more per stage)
@@ -994,12 +1087,12 @@ bool big_tiles(int64_t max_rows, int E, int K) { return max_rows >= 128 * (int64
 // The tile list is set up with one thread per expert, so E <= 128.
 bool small_tiles(int64_t max_rows, int E) { return max_rows <= 64 * (int64_t)E && E <= 128; }
 
-// Tall 256-row tiles for the plain products (the down projection) when the
-// experts hold at most 384 rows on average: an expert then has one or two
-// tiles, and a second tile of a few rows would cost about half a full one
-// (measured on the 128-expert layer: down 881 -> 743 us).  With more rows per
-// expert such tails are rare and the always-issued extra load costs more
-// than it saves (down 74 -> 86 us at 512 rows per expert).
+// Tall 256-row tiles for the down and gate/up projections when the experts
+// hold at most 384 rows on average: an expert then has one or two tiles, and
+// a second tile of a few rows would cost about half a full one (measured on
+// the 128-expert layer: down 881 -> 743 us, gate/up 1470 -> 1259 us).  With
+// more rows per expert such tails are rare and the always-issued extra load
+// costs more than it saves (down 74 -> 86 us at 512 rows per expert).
 bool tall_tiles(int64_t max_rows, int E) { return max_rows <= 384 * (int64_t)E; }
 
 template <int EPI, bool BT>
@@ -1010,6 +1103,11 @@ hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows
     if (big_tiles(max_rows, E, K) && tall_tiles(max_rows, E) && row_token == nullptr)
       return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, nullptr,
                                                              0, out2, aux, 1, nullptr, sched);
+  }
+  if constexpr (EPI == kEpiSwiglu && !BT) {
+    if (big_tiles(max_rows, E, K) && tall_tiles(max_rows, E))
+      return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
+                                                             a_rows, out2, aux, 1, nullptr, sched);
   }
   if (big_tiles(max_rows, E, K))
     return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
