@@ -615,8 +615,98 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     int elane;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(elane));
     const int lr = elane % 32, lc = 4 * (elane / 32);
+    // silu(g) u for two outputs, packed: silu(g) = g / (1 + e^-g) with the
+    // hardware reciprocal (about 1 ulp in float32, far below the bf16
+    // rounding of h)
+    auto swiglu2 = [](float g0, float u0, float g1, float u1) {
+      return pack_bf16x2(g0 * __builtin_amdgcn_rcpf(1.f + __expf(-g0)) * u0,
+                         g1 * __builtin_amdgcn_rcpf(1.f + __expf(-g1)) * u1);
+    };
+    // With two 4-column groups 8 columns apart in each of lanes l and l + 32
+    // (the same row), one lane swap (v_permlane32_swap) gives lane l the
+    // first group's 8 consecutive columns and lane l + 32 the second's: one
+    // 16-byte store per lane instead of two 8-byte ones.  pk[g][w] is dword w
+    // of group g; every lane takes part in the swap.
+    auto swap_store = [&](uint32_t (&pk)[2][2], bf16_t* orow, int c, bool ok) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(pk[0][w], pk[1][w], false, false);
+        pk[0][w] = sw[0];
+        pk[1][w] = sw[1];
+      }
+      if (ok) *(uint4*)(orow + c) = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);
+    };
+    if constexpr (EPI == kEpiSwiglu) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (64 * wm + 32 * i >= t.rows) continue;  // (wave-uniform: the whole block is past the rows)
+        const int r = 64 * wm + 32 * i + lr;
+        bf16_t* orow = Out + (t.row0 + r) * N;
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            // groups q4 = 2 p, 2 p + 1 (columns 8 q4 + lc + 0..3)
+            uint32_t pk[2][2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                const int q = 4 * (2 * p + g) + 2 * w;
+                pk[g][w] = swiglu2(acc[j][i][q], acc[j + NJ / 2][i][q], acc[j][i][q + 1], acc[j + NJ / 2][i][q + 1]);
+              }
+            const int c = t.n0 + (WCOL / 2) * wn + 32 * j + 16 * p + 2 * lc;
+            swap_store(pk, orow, c, r < t.rows && c < N);
+          }
+      }
+    } else if constexpr (EPI == kEpiPlain || EPI == kEpiScatter) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (64 * wm + 32 * i >= t.rows) continue;  // (wave-uniform)
+        const int r = 64 * wm + 32 * i + lr;
+        bf16_t* orow = Out + (t.row0 + r) * N;
+        bool ok = r < t.rows;
+        float wr = 0.f;
+        if constexpr (EPI == kEpiScatter) {
+          // the row's token gets the row rounded to bf16 times its routing
+          // weight, rounded again (what the combine computes for one pair);
+          // the index slot holds zeros past the tile's rows
+          const int tok = s_rt[slot][r];
+          wr = s_rw[slot][r];
+          ok = ok && tok >= 0 && tok < a_rows;
+          orow = Out + (int64_t)(ok ? tok : 0) * N;
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            uint32_t pk[2][2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const int q = 4 * (2 * p + g);
+              const uint2 y = make_uint2(pack_bf16x2(acc[j][i][q], acc[j][i][q + 1]),
+                                         pack_bf16x2(acc[j][i][q + 2], acc[j][i][q + 3]));
+              if constexpr (EPI == kEpiScatter) {
+                float f[4];
+                unpack4(y, f);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) f[v] = fmaf(wr, f[v], 0.f);
+                const uint2 z = pack4(f);
+                pk[g][0] = z.x;
+                pk[g][1] = z.y;
+              } else {
+                pk[g][0] = y.x;
+                pk[g][1] = y.y;
+              }
+            }
+            const int c = t.n0 + WCOL * wn + 32 * j + 16 * p + 2 * lc;
+            swap_store(pk, orow, c, ok && c < N);
+          }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      if (EPI == kEpiSwiglu || EPI == kEpiPlain || EPI == kEpiScatter) break;
       const int r = 64 * wm + 32 * i + lr;
       if (r >= t.rows) continue;
       bf16_t* orow = Out + (t.row0 + r) * N;
@@ -743,36 +833,35 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       // the extra rows: acc_x holds row BM + lane % 32, the wave's wm-th
       // column block
       const int r = BM + lr;
-      if (SWIGLU && t.rows > BM && r < t.rows) {
+      if (SWIGLU && t.rows > BM) {
         // acc_x[4 q4 + v] is gate column (WCOL / 2) wn + 16 wm + 8 q4 + lc + v
         // for q4 < 2 and the matching up column for q4 + 2
         bf16_t* orow = Out + (t.row0 + r) * N;
+        uint32_t pk[2][2];
 #pragma unroll
-        for (int q4 = 0; q4 < 2; ++q4) {
-          const int c = t.n0 + (WCOL / 2) * wn + 16 * wm + 8 * q4 + lc;
-          if (c >= N) continue;
-          uint32_t packed[2];
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            float hv[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const float gt = acc_x[4 * q4 + 2 * h2 + u], up = acc_x[4 * (q4 + 2) + 2 * h2 + u];
-              hv[u] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
-            }
-            packed[h2] = pack_bf16x2(hv[0], hv[1]);
+          for (int w = 0; w < 2; ++w) {
+            const int q = 4 * g + 2 * w;
+            pk[g][w] = swiglu2(acc_x[q], acc_x[q + 8], acc_x[q + 1], acc_x[q + 9]);
           }
-          *(uint2*)(orow + c) = make_uint2(packed[0], packed[1]);
-        }
-      } else if (!SWIGLU && t.rows > BM && r < t.rows) {
+        const int c = t.n0 + (WCOL / 2) * wn + 16 * wm + 2 * lc;
+        swap_store(pk, orow, c, r < t.rows && c < N);
+      } else if (!SWIGLU && t.rows > BM) {
+        // the wave's wm-th column block
         bf16_t* orow = Out + (t.row0 + r) * N;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = t.n0 + WCOL * wn + 32 * wm + 8 * q4 + lc;
-          if (c >= N) continue;
-          const uint32_t p0 = pack_bf16x2(acc_x[4 * q4], acc_x[4 * q4 + 1]);
-          const uint32_t p1 = pack_bf16x2(acc_x[4 * q4 + 2], acc_x[4 * q4 + 3]);
-          *(uint2*)(orow + c) = make_uint2(p0, p1);
+        for (int p = 0; p < 2; ++p) {
+          uint32_t pk[2][2];
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const int q = 4 * (2 * p + g) + 2 * w;
+              pk[g][w] = pack_bf16x2(acc_x[q], acc_x[q + 1]);
+            }
+          const int c = t.n0 + WCOL * wn + 32 * wm + 16 * p + 2 * lc;
+          swap_store(pk, orow, c, r < t.rows && c < N);
         }
       }
     }
