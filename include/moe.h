@@ -139,7 +139,11 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, in
  *       bf16 only, and x_rows * d below 2^30; row_token as moe_permute
  *       writes it).
  *   moe_down_proj:       y_perm[r] = h[r] @ Wd[e]
- * Neither needs a workspace.                                                  */
+ * Neither needs a workspace.  Without one, the down projection computes every
+ * tile whole; moe_grouped_ffn and moe_forward use their workspace to cut the
+ * k-range of a last, partial round of 256-row tiles into pieces whose float32
+ * partial sums are added in a fixed order -- deterministic, but those rows
+ * can differ from moe_down_proj's in the last bit.                          */
 moe_status moe_gate_up_swiglu(const void* x, const int32_t* expert_offsets, int32_t max_rows,
                               int32_t E, int32_t d, int32_t I, const void* w_gate_up, moe_dtype dt,
                               const int32_t* row_token, int32_t x_rows, void* h, void* stream);

@@ -9,6 +9,8 @@ the same launch configuration the benchmark times.
 """
 import gc
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -285,6 +287,41 @@ def test_grouped_ffn_tall_tiles(tre, counts):
     check_grouped_ffn(tre, inp, idx)
 
 
+# Experts of 1024 rows fill 4 row tiles each and the two of 1100 rows 5: 34
+# row tiles x 8 column tiles (d = 2048) = 272 tiles of 256 rows on a grid
+# capped at 256 workgroups (one per CU).  The down projection cuts the last
+# 16 into 4 ranges of k-stages (K = 1024: 32 stages), whose partial tiles a
+# second kernel adds in order.
+SPLIT_TAIL_COUNTS = (1024, 1024, 1024, 1024, 1024, 1024, 1100, 1100)
+
+
+def split_tail_inputs():
+    counts = np.array(SPLIT_TAIL_COUNTS)
+    E, T = len(counts), int(counts.sum())
+    inp = workloads.make_custom(T=T, d=2048, E=E, k=1, I=1024, dtype="bf16", seed=T, logits="normal",
+                                name="split_tail")
+    idx = np.random.default_rng(T).permutation(np.repeat(np.arange(E, dtype=np.int32), counts))
+    return inp, idx
+
+
+def test_grouped_ffn_split_tail(tre):
+    # the grouped feed-forward (its workspace holds the tail) against the oracle, every grouped row
+    inp, idx = split_tail_inputs()
+    say(f"grouped ffn split tail, counts {list(SPLIT_TAIL_COUNTS)}")
+    check_grouped_ffn(tre, inp, idx.reshape(-1, 1))
+
+
+def test_forward_split_tail_one_pair_per_token(tre):
+    # one pair per token: the split tail's sum writes the output rows; the
+    # layer equals the entry points bit for bit, and every token the oracle
+    inp, idx = split_tail_inputs()
+    w = np.random.default_rng(inp.T + 1).uniform(0.05, 1.0, inp.T).astype(np.float32)
+    inp = dataclasses.replace(inp, logits=None, pair_expert=idx, pair_w=w)
+    say("forward split tail, one pair per token")
+    check_fused_equals_staged(tre, inp)
+    check_forward(tre, inp)
+
+
 def test_grouped_ffn_empty_experts(tre):
     inp = workloads.make_custom(T=200, d=128, E=16, k=2, I=128, dtype="bf16", seed=5, logits="normal")
     idx = np.where(np.arange(400).reshape(200, 2) % 2 == 0, 3, 11).astype(np.int32)   # only experts 3, 11
@@ -465,10 +502,13 @@ def test_forward_small_bf16(tre):
 
 
 def check_fused_equals_staged(tre, inp):
-    """moe_forward (workspace filled with NaN bytes, claimed-tail tickets, and
-    for one pair per token the down projection writing the output rows) equals
-    the entry points run one after the other, bit for bit on every row, at
-    the workload's full size and launch configuration."""
+    """moe_forward (workspace filled with NaN bytes, claimed-tail tickets, the
+    split tail of the down projection, and for one pair per token the down
+    projection writing the output rows) equals the entry points run one after
+    the other -- grouping with the row moves, the grouped feed-forward (with
+    its workspace: the same tiles, tail and all), combine -- bit for bit on
+    every row, at the workload's full size and launch configuration.  The
+    separate projections (no workspace, whole tiles) agree within rounding."""
     torch = _torch()
     T, d, E, k, I = inp.T, inp.d, inp.E, inp.k, inp.I
     xd, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
@@ -483,16 +523,21 @@ def check_fused_equals_staged(tre, inp):
         w = to_device(inp.pair_w.reshape(T, k))
         tre.moe_forward(xd, wgu, wd, k, topk_idx=idx, topk_w=w, out=out, workspace=ws)
     sync()
-    _, row_token, pair_row, offsets = tre.moe_permute(xd, idx.reshape(-1), k, E, move_rows=False)
-    h = tre.moe_gate_up_swiglu(xd, offsets, wgu, row_token=row_token, max_rows=T * k)
-    y = tre.moe_down_proj(h, offsets, wd)
+    x_perm, row_token, pair_row, offsets = tre.moe_permute(xd, idx.reshape(-1), k, E)
+    y = tre.moe_grouped_ffn(x_perm, offsets, wgu, wd)
     staged = tre.moe_combine(y, pair_row, w.reshape(-1), T, k)
     sync()
     same = torch.all(out.view(torch.int16) == staged.view(torch.int16), dim=1)
     n_bad = int((~same).sum())
     say(f"  {inp.name}: fused vs staged, {n_bad} of {T} rows differ")
     assert n_bad == 0
-    del xd, wgu, wd, ws, out, h, y, staged
+    del x_perm, y, staged
+    h = tre.moe_gate_up_swiglu(xd, offsets, wgu, row_token=row_token, max_rows=T * k)
+    y = tre.moe_down_proj(h, offsets, wd)
+    sep = tre.moe_combine(y, pair_row, w.reshape(-1), T, k)
+    sync()
+    check_outputs(to_host(sep), as_f64(to_host(out)), 1e-2, label="separate projections vs fused")
+    del xd, wgu, wd, ws, out, h, y, sep
 
 
 def test_forward_large_e128(tre):

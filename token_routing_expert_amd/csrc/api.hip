@@ -54,7 +54,7 @@ ForwardLayout forward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
   L.h = o;         o += align256(P * I * s);
   L.y_perm = o;    o += align256(P * d * s);
   L.perm_ws = o;   o += permute_index_workspace(P, (int)E);
-  L.split = o;     o += dt == MOE_BF16 ? align256(split_workspace(P, d)) : 0;
+  L.split = o;     o += dt == MOE_BF16 ? align256(split_workspace(P, (int)E, (int)d, (int)I)) : 0;
   L.sched = o;     o += dt == MOE_BF16 ? align256(kSchedWords * 4) : 0;
   L.row_w = o;     o += dt == MOE_BF16 && k == 1 ? align256(P * 4) : 0;
   L.total = o;
@@ -82,7 +82,7 @@ BackwardLayout backward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64
   L.dy = o;        o += align256(P * d * 2);
   L.dgu = o;       o += align256(P * 2 * I * 2);
   L.dxp = o;       o += align256(P * d * 2);
-  L.split = o;     o += align256(split_workspace(P, d));
+  L.split = o;     o += align256(split_workspace(P, (int)E, (int)d, (int)I));
   L.sched = o;     o += align256(kSchedWords * 4);
   L.total = o;
   return L;
@@ -158,12 +158,11 @@ moe_status moe_permute(const void* x, moe_dtype dt, int32_t T, int32_t d, int32_
 }
 
 size_t moe_grouped_ffn_workspace_size(int32_t max_rows, int32_t E, int32_t d, int32_t I, moe_dtype dt) {
-  (void)E;
-  if (max_rows < 0 || I < 1 || !dtype_ok(dt)) return 0;
-  // h, then (bf16) the down projection's k-split partial sums (few rows) and
-  // the two products' tile counters
+  if (max_rows < 0 || I < 1 || E < 1 || !dtype_ok(dt)) return 0;
+  // h, then (bf16) the down projection's k-split partial sums (few rows) or
+  // split-tail partial tiles (many), and the two products' tile counters
   return align256((size_t)max_rows * I * elem_size(dt)) +
-         (dt == MOE_BF16 && d > 0 ? align256(split_workspace(max_rows, d)) + align256(kSchedWords * 4) : 0);
+         (dt == MOE_BF16 && d > 0 ? align256(split_workspace(max_rows, E, d, I)) + align256(kSchedWords * 4) : 0);
 }
 
 moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, int32_t max_rows, int32_t E,
@@ -182,7 +181,7 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, in
   hipStream_t s = (hipStream_t)stream;
   if (dt == MOE_BF16) {
     char* split = (char*)workspace + align256((size_t)max_rows * I * 2);
-    int32_t* sched = (int32_t*)(split + align256(split_workspace(max_rows, d)));
+    int32_t* sched = (int32_t*)(split + align256(split_workspace(max_rows, E, d, I)));
     TRY(from_hip(launch_sched_reset(sched, s)));
     return from_hip(launch_grouped_ffn_bf16((const bf16_t*)x_perm, expert_offsets, max_rows, E, d, I,
                                             (const bf16_t*)w_gate_up, (const bf16_t*)w_down, (bf16_t*)workspace,

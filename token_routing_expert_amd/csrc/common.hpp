@@ -176,10 +176,11 @@ hipError_t launch_sched_reset(int32_t* sched, hipStream_t s);
 hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s,
                                const int32_t* row_token = nullptr, int64_t x_rows = 0, int32_t* sched = nullptr);
-// split_ws (optional, split_workspace(max_rows, d) bytes, float32): with few
-// rows the down projection's k-stages are split over more workgroups and
-// summed there in a fixed order (deterministic).
-size_t split_workspace(int64_t max_rows, int d);
+// split_ws (optional, split_workspace(max_rows, E, d, I) bytes, float32):
+// with few rows the down projection's k-stages are split over more
+// workgroups and summed there in a fixed order (deterministic); with many,
+// the tiles of a last, partial round of 256-row tiles are (the split tail).
+size_t split_workspace(int64_t max_rows, int E, int d, int I);
 // One pair per token (k = 1): the down projection can write the layer output
 // itself, out[row_token[r]] = row_w[r] * bf16(y[r]) rounded to bf16 (what
 // the combine computes for a single pair), from its 256-row tiles or its

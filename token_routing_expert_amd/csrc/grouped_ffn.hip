@@ -106,6 +106,18 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
 // XOR-swizzled instead of padded, so that the activation reads
 // (ds_read_b128 of 16 consecutive rows) and the transposing weight reads (4
 // consecutive k-rows x 32 bytes per 16-lane group) touch every bank once.
+
+// Split-tail workspace of the ping-pong down projection (float32 words):
+// a header (split tiles, pieces per tile), one 4-word record per split tile
+// (expert, first row, rows, first column) and kTailPieces partial tiles of
+// up to 288 rows (256 + the 32 extra rows of a tall tile) x 256 columns.
+constexpr int kTailMaxSplit = 4;   // pieces per split tile, at most
+constexpr int kTailPieces = 256;   // pieces in flight, at most
+constexpr int kTailHdrWords = 64;
+constexpr int kTailPartOff = kTailHdrWords + 4 * kTailPieces;
+constexpr int kTailPieceFloats = 288 * 256;
+constexpr size_t kTailBytes = ((size_t)kTailPartOff + (size_t)kTailPieces * kTailPieceFloats) * 4;
+
 namespace dma {
 
 
@@ -167,8 +179,11 @@ template <int EPI, bool BT, int BK, int OCC, int NJ, int WM, int NS, bool PP, bo
 __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K, int N, int ldw,
     const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles, const int32_t* __restrict__ row_token,
-    int64_t a_rows, bf16_t* __restrict__ Out2, const bf16_t* __restrict__ Aux, int n_split,
+    int64_t a_rows, bf16_t* __restrict__ Out2, const bf16_t* __restrict__ Aux, int n_split_arg,
     float* __restrict__ Part, int32_t* __restrict__ sched, const float* __restrict__ row_w) {
+  // (k-split ranges are only used with the lockstep tiles: the ping-pong
+  // instances see one range per tile, a constant)
+  const int n_split = PP ? 1 : n_split_arg;
   // gate/up tiles: 128 gate columns and the matching 128 up columns
   constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   static_assert(!(SWIGLU && BT), "the gate/up weight is only read as [K][2N]");
@@ -241,14 +256,58 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   const int64_t total_tiles = (int64_t)total_mt * n_tiles;
   const int G = gridDim.x;
   const int vb = (blockIdx.x % kXcd) * (G / kXcd) + blockIdx.x / kXcd;
+  const int nk = K / BK;
+  // Split tail (the ping-pong down projection, with Part pointing to a tail
+  // workspace, whole tiles otherwise): when the tiles fill whole rounds of
+  // the grid but for t_exc <= G / 2 of them, those last tiles would make a
+  // round of their own, with most workgroups idle.  Each is cut instead into
+  // tS ranges of k-stages (pieces); a piece writes its float32 partial tile
+  // to the workspace, and k_tail_sum adds the pieces of every such tile in
+  // order (deterministic) and applies the epilogue.
+  constexpr bool TAIL = PP && !BT && (EPI == kEpiPlain || EPI == kEpiScatter);
+  int tS = 1;
+  int64_t t_full = total_tiles, t_exc = 0;
+  if (TAIL && Part != nullptr && n_split == 1 && total_tiles > G && total_tiles % G != 0) {
+    const int64_t exc = total_tiles % G;
+    const int64_t sp = min<int64_t>(min<int64_t>(kTailMaxSplit, G / exc),
+                                    min<int64_t>(kTailPieces / exc, nk / (2 * NS)));
+    if (sp >= 2) {
+      tS = (int)sp;
+      t_exc = exc;
+      t_full = total_tiles - exc;
+    }
+  }
+  if (TAIL && Part != nullptr && blockIdx.x == 0 && tid == 0) {
+    int32_t* hdr = (int32_t*)Part;
+    hdr[0] = (int)t_exc;
+    hdr[1] = tS;
+  }
   // Work units: each tile's k-stages cut into n_split ranges (1: whole
-  // tiles), unit u = tile u / n_split, range u % n_split; consecutive units
-  // (one tile's ranges) go to workgroups of one XCD.
-  const int64_t total_units = total_tiles * n_split;
+  // tiles), unit u = tile u / n_split, range u % n_split; or whole tiles
+  // followed by the pieces of the split tail.  Consecutive units (one
+  // tile's ranges) go to workgroups of one XCD.
+  const int64_t total_units = tS > 1 ? t_full + t_exc * tS : total_tiles * n_split;
   if (vb >= total_units) return;  // the whole workgroup: no barrier follows
   const int my_tiles = (int)((total_units - vb + G - 1) / G);  // units of this workgroup
-  const int nk = K / BK;
   auto k_begin = [&](int split) { return split * nk / n_split; };
+  // unit u: its tile, its range of k-stages [k0, k1), and its piece of a
+  // split tail tile (-1: a whole tile or an n_split range)
+  auto unit_tile = [&](int64_t u) -> int64_t {
+    if (TAIL && tS > 1 && u >= t_full) return t_full + (int)(u - t_full) / tS;
+    return u / n_split;
+  };
+  auto unit_range = [&](int64_t u, int& k0, int& k1) {
+    if (TAIL && tS > 1 && u >= t_full) {
+      const int pc = (int)(u - t_full) % tS;
+      k0 = pc * nk / tS;
+      k1 = (pc + 1) * nk / tS;
+      return pc;
+    }
+    const int sp = (int)(u % n_split);
+    k0 = k_begin(sp);
+    k1 = k_begin(sp + 1);
+    return -1;
+  };
   // Claimed tail (ping-pong tiles, whole tiles, sched != nullptr, at least
   // four rounds of tiles): the first rs = rounds - 1 tiles of every
   // workgroup are dealt round-robin as above; the rest, units rs G ..
@@ -265,8 +324,9 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   int total_stages = 0;
   if (!dyn) {
     for (int i = 0; i < my_tiles; ++i) {
-      const int split = (int)((vb + (int64_t)i * G) % n_split);
-      total_stages += k_begin(split + 1) - k_begin(split);
+      int k0, k1;
+      unit_range(vb + (int64_t)i * G, k0, k1);
+      total_stages += k1 - k0;
     }
   } else {
     // tile 0 (dealt); later tiles count in as they become known.  rs >= 3, so
@@ -313,8 +373,8 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   // (rows * K < 2^31 is checked on the host).
   int i_tile = 0, i_k = 0, i_len = 0;
   int i_cursor = 0;
-  Tile inext = decode(vb / n_split, i_cursor);  // the tile the issue side enters next
-  int inext_split = vb % n_split;
+  Tile inext = decode(unit_tile(vb), i_cursor);  // the tile the issue side enters next
+  int64_t inext_u = vb;                           // and its unit
   int total = total_stages;  // stages of the tiles known so far
   // Claiming a ticket (wave 0, one lane): the atomic's return lands in
   // `ticket` asynchronously and is counted by vmcnt in issue order with the
@@ -456,17 +516,20 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       }
       b_voff[p] = ok ? (uint32_t)(kr * ldw + gcol) * 2u : kOutOfRange;
     }
-    const int k0 = k_begin(inext_split);
+    int k0, k1;
+    unit_range(inext_u, k0, k1);
     ka = (uint32_t)k0 * kAStep;
     kb = (uint32_t)k0 * kb_step;
-    i_len = k_begin(inext_split + 1) - k0;
+    i_len = k1 - k0;
     const int64_t u = unit_of(i_tile + 1);
     if (u >= 0) {
-      inext = decode(u / n_split, i_cursor);
-      inext_split = (int)(u % n_split);
+      inext = decode(unit_tile(u), i_cursor);
+      inext_u = u;
       if (row_token) index_dma(inext, (i_tile + 1) % NSLOT);
       if (dyn) {
-        total += nk;
+        int u0, u1;
+        unit_range(u, u0, u1);
+        total += u1 - u0;
         if (i_tile + 2 >= rs) claim(i_tile + 2);
       }
     }
@@ -867,6 +930,43 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     }
   };
 
+  // A piece of a split tail tile: its float32 partial tile (the tile's rows,
+  // all BNB columns, tall rows included) goes to piece slot xt tS + piece
+  // of the tail workspace; piece 0 records where the tile lies.
+  auto tail_piece = [&](const Tile& t, int64_t xt, int piece) {
+    if constexpr (TAIL) {
+      static_assert(BM + XR <= 288 && BNB == 256, "the tail workspace holds 288 x 256 partial tiles");
+      int elane;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(elane));
+      const int lr = elane % 32, lc = 4 * (elane / 32);
+      if (piece == 0 && tid == 0) {
+        int32_t* rec = (int32_t*)Part + kTailHdrWords + 4 * xt;
+        rec[0] = t.e;
+        rec[1] = (int)t.row0;
+        rec[2] = t.rows;
+        rec[3] = t.n0;
+      }
+      float* pt = Part + kTailPartOff + ((int64_t)xt * tS + piece) * kTailPieceFloats;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 64 * wm + 32 * i + lr;
+        if (r >= t.rows) continue;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *(f32x4*)(pt + r * BNB + WCOL * wn + 32 * j + 8 * q4 + lc) =
+                f32x4{acc[j][i][4 * q4], acc[j][i][4 * q4 + 1], acc[j][i][4 * q4 + 2], acc[j][i][4 * q4 + 3]};
+      }
+      if (TALL && t.rows > BM && BM + lr < t.rows) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(f32x4*)(pt + (BM + lr) * BNB + WCOL * wn + 32 * wm + 8 * q4 + lc) =
+              f32x4{acc_x[4 * q4], acc_x[4 * q4 + 1], acc_x[4 * q4 + 2], acc_x[4 * q4 + 3]};
+      }
+    }
+  };
+
   // ---- the stage stream ----
   // Stage g of the stream lives in ring slot g % NS.  The compute side walks
   // its tiles; within a tile the stages run through NS copies of the stage
@@ -894,8 +994,8 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
 
   int g = 0;
   int c_cursor = 0;
-  Tile cur = decode(vb / n_split, c_cursor);
-  int cur_split = vb % n_split;
+  Tile cur = decode(unit_tile(vb), c_cursor);
+  int64_t cur_u = vb;
   Frag f0, f1;
   zero_acc();
 
@@ -980,7 +1080,9 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     constexpr bool kKeepPace = PP && (EPI == kEpiPlain || EPI == kEpiScatter);
     const bool active = kKeepPace || 64 * wm < cur.rows;
     cur_tall = TALL && cur.rows > BM;
-    int left = k_begin(cur_split + 1) - k_begin(cur_split);
+    int cur_k0, cur_k1;
+    const int cur_piece = unit_range(cur_u, cur_k0, cur_k1);
+    int left = cur_k1 - cur_k0;
     // the unrolled ring, entered at the slot of the tile's first stage: the
     // copies before it are skipped in the first round only (one entry, so
     // the loop stays reducible and its control flow uniform)
@@ -999,12 +1101,15 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       }
       first = 0;
     }
-    epilogue(cur, cur_split, c_tile % NSLOT);
+    if (TAIL && cur_piece >= 0)
+      tail_piece(cur, unit_tile(cur_u) - t_full, cur_piece);
+    else
+      epilogue(cur, (int)(cur_u % n_split), c_tile % NSLOT);
     zero_acc();
     const int64_t u = unit_of(c_tile + 1);
     if (u < 0) break;
-    cur = decode(u / n_split, c_cursor);
-    cur_split = (int)(u % n_split);
+    cur = decode(unit_tile(u), c_cursor);
+    cur_u = u;
   }
   if constexpr (PP) {
     if (wave < 4) barrier();
@@ -1138,6 +1243,51 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
   *(uint2*)(out + t * N + c) = pack4(f);
 }
 
+// The split tail's sums: block (x, y) takes rows 4 y .. 4 y + 3 of split
+// tile x, one thread per 4 columns; it adds the tile's pieces in piece order
+// (deterministic) and applies the down projection's epilogue -- the row
+// rounded to bf16, or with row_token (one pair per token) that times the
+// row's routing weight, rounded again, into its token's row of out.  The
+// header says how many tiles were split (none: every block returns).
+constexpr int kTailSumRows = 4;
+__global__ __launch_bounds__(256) void k_tail_sum(const float* __restrict__ ws, int N, bf16_t* __restrict__ out,
+                                                  const int32_t* __restrict__ row_token,
+                                                  const float* __restrict__ row_w, int64_t out_rows) {
+  const int32_t* hdr = (const int32_t*)ws;
+  const int n_exc = hdr[0], n_pc = hdr[1];
+  const int b = blockIdx.x;
+  if (b >= n_exc) return;
+  const int32_t* rec = hdr + kTailHdrWords + 4 * b;
+  const int64_t row0 = rec[1];
+  const int rows = rec[2], n0 = rec[3];
+  const int r = kTailSumRows * blockIdx.y + threadIdx.x / 64, c = 4 * (threadIdx.x % 64);
+  if (r >= rows || n0 + c >= N) return;
+  {
+    const float* part = ws + kTailPartOff + (int64_t)b * n_pc * kTailPieceFloats + r * 256 + c;
+    f32x4 p[kTailMaxSplit];
+#pragma unroll
+    for (int pc = 0; pc < kTailMaxSplit; ++pc)
+      if (pc < n_pc) p[pc] = *(const f32x4*)(part + (int64_t)pc * kTailPieceFloats);
+    f32x4 sum = p[0];
+#pragma unroll
+    for (int pc = 1; pc < kTailMaxSplit; ++pc)
+      if (pc < n_pc) sum += p[pc];
+    const uint2 y = make_uint2(pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3]));
+    if (!row_token) {
+      *(uint2*)(out + (row0 + r) * N + n0 + c) = y;
+      return;
+    }
+    const int64_t t = row_token[row0 + r];
+    if (t < 0 || t >= out_rows) return;
+    const float w = row_w[row0 + r];
+    float f[4];
+    unpack4(y, f);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) f[v] = fmaf(w, f[v], 0.f);
+    *(uint2*)(out + t * N + n0 + c) = pack4(f);
+  }
+}
+
 // Ranges per tile for a product with few rows (1: no split).  Tiles are
 // counted for the worst case of the offsets (every expert non-empty); the
 // split that needs the fewest rounds of CU slots per unit of work wins.
@@ -1162,7 +1312,7 @@ template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
                        int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr,
-                       int32_t* sched = nullptr);
+                       int32_t* sched = nullptr, float* tail_ws = nullptr);
 
 // 256-row tiles (8 waves in ping-pong, one workgroup per CU: each weight
 // stage feeds twice the rows) once the experts hold 128 rows or more on
@@ -1187,11 +1337,11 @@ bool tall_tiles(int64_t max_rows, int E) { return max_rows <= 384 * (int64_t)E; 
 template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token, int64_t a_rows,
-                       bf16_t* out2, const bf16_t* aux, int32_t* sched) {
+                       bf16_t* out2, const bf16_t* aux, int32_t* sched, float* tail_ws) {
   if constexpr (EPI == kEpiPlain && !BT) {
     if (big_tiles(max_rows, E, K) && tall_tiles(max_rows, E) && row_token == nullptr)
       return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, nullptr,
-                                                             0, out2, aux, 1, nullptr, sched);
+                                                             0, out2, aux, 1, tail_ws, sched);
   }
   if constexpr (EPI == kEpiSwiglu && !BT) {
     if (big_tiles(max_rows, E, K) && tall_tiles(max_rows, E))
@@ -1200,7 +1350,8 @@ hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows
   }
   if (big_tiles(max_rows, E, K))
     return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
-                                                     a_rows, out2, aux, 1, nullptr, sched);
+                                                     a_rows, out2, aux, 1, EPI == kEpiPlain && !BT ? tail_ws : nullptr,
+                                                     sched);
   if (small_tiles(max_rows, E))
     return launch_dma<EPI, BT, 32, 2, 4, 1, 3, false>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
                                                       a_rows, out2, aux);
@@ -1225,8 +1376,17 @@ hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, i
                                         x_rows, nullptr, nullptr, sched);
 }
 
-size_t split_workspace(int64_t max_rows, int d) {
-  return max_rows <= kSplitMaxRows ? (size_t)kSplitMax * max_rows * d * sizeof(float) : 0;
+// Whether the 256-row down projection can have a split tail: only when its
+// persistent grid is capped at the CU count (otherwise every tile has a
+// workgroup of its own, whatever the offsets).
+bool down_tail_possible(int64_t max_rows, int E, int d, int I) {
+  const int64_t max_mt = max_rows / 256 + (E < max_rows ? E : max_rows);
+  return max_rows > kSplitMaxRows && big_tiles(max_rows, E, I) && max_mt * ceil_div(d, 256) > (int64_t)num_cus();
+}
+
+size_t split_workspace(int64_t max_rows, int E, int d, int I) {
+  if (max_rows <= kSplitMaxRows) return (size_t)kSplitMax * max_rows * d * sizeof(float);
+  return down_tail_possible(max_rows, E, d, I) ? kTailBytes : 0;
 }
 
 int down_split(int64_t max_rows, int E, int d, int I, bool have_split_ws) {
@@ -1260,12 +1420,20 @@ hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int6
     }
   }
   int32_t* dn_sched = sched ? sched + kSchedDown : nullptr;
+  // the split tail (256-row tiles, with a workspace, when the grid is capped)
+  float* tail_ws = split_ws && down_tail_possible(max_rows, E, d, I) ? split_ws : nullptr;
+  hipError_t e;
   if (sc)   // 256-row tiles (down_scatters)
-    return launch_dma<kEpiScatter, false, 32, 1, 4, 4, 4, true>(h, expert_offsets, max_rows, E, I, d, d, w_down,
-                                                                 sc->out, s, sc->row_token, sc->T, nullptr, nullptr,
-                                                                 1, nullptr, dn_sched, sc->row_w);
-  return launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s, nullptr, 0,
-                                       nullptr, nullptr, dn_sched);
+    e = launch_dma<kEpiScatter, false, 32, 1, 4, 4, 4, true>(h, expert_offsets, max_rows, E, I, d, d, w_down,
+                                                              sc->out, s, sc->row_token, sc->T, nullptr, nullptr, 1,
+                                                              tail_ws, dn_sched, sc->row_w);
+  else
+    e = launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s, nullptr, 0,
+                                      nullptr, nullptr, dn_sched, tail_ws);
+  if (e != hipSuccess || tail_ws == nullptr) return e;
+  k_tail_sum<<<dim3(kTailPieces / 2, 288 / kTailSumRows), 256, 0, s>>>(
+      tail_ws, d, sc ? sc->out : y_perm, sc ? sc->row_token : nullptr, sc ? sc->row_w : nullptr, sc ? sc->T : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_gate_up_save_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
