@@ -578,7 +578,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   struct Frag {
     bf16x8 a[2], b[NJ];
     bf16x8 ax;  // tall tiles: the extra rows
-    bf16x8 bx;  // tall gate/up tiles: 16 gate columns and their 16 up columns
+    bf16x8 bx;  // tall tiles: the weight fragment of the extra rows
   };
   // Per-lane LDS addresses of this wave's fragment reads in ring slot 0 at
   // k-step 0.  Every read of the stage loop sits a constant offset from one
@@ -614,6 +614,13 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     const int col = (WCOL / 2) * wn + 16 * wm + (g16 % 2) * (BNB / 2) + 4 * (L % 4);
     fbx = lds_address(sB) + GE::b_byte(kr, col >> 3) + ((col >> 2) & 1) * 8;
     asm("" : "+v"(fbx));
+  } else if constexpr (TALL) {
+    // the wave's wm-th column block (selected without indexing the bases at
+    // run time, which would put them in scratch memory)
+    fbx = fb[0];
+#pragma unroll
+    for (int j = 1; j < NFB; ++j) fbx = wm == j ? fb[j] : fbx;
+    asm("" : "+v"(fbx));
   }
   typedef __attribute__((address_space(3))) const char lds_char;
   auto lds_at = [](uint32_t a) { return (lds_char*)(uintptr_t)a; };
@@ -640,12 +647,14 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       const bool up = SWIGLU && j >= NJ / 2;  // the up half: BNB / 2 columns = BNB bytes on
       f.b[j] = read_b(fb[up ? j - NJ / 2 : j], B_OFF + ks * 16 * GE::BROW + (up ? BNB : 0));
     }
-    if constexpr (TALL) {
-      if (cur_tall) {
-        f.ax = read_a(fax[ks], A_OFF);
-        if constexpr (SWIGLU) f.bx = read_b(fbx, B_OFF + ks * 16 * GE::BROW);
-      }
-    }
+  };
+  // tall tiles: the extra rows' fragment and the weight fragment it meets
+  // (gate/up: 16 gate and their 16 up columns; down: the wm-th column
+  // block, read a second time), after the stage's other reads
+  auto read_x = [&](auto slot_c, int ks, Frag& f) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    f.ax = read_a(fax[ks], SLOT * A_STAGE);
+    f.bx = read_b(fbx, SLOT * GE::B_BYTES + ks * 16 * GE::BROW);
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
@@ -653,21 +662,10 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
-    if constexpr (TALL) {
-      if (cur_tall) {
-        if constexpr (SWIGLU) {
-          acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.bx, f.ax, acc_x, 0, 0, 0);
-        } else {
-          // the wm-th column block, selected without indexing the fragments
-          // at run time (which would put them in scratch memory)
-          bf16x8 bw = f.b[0];
-#pragma unroll
-          for (int j = 1; j < NJ; ++j) bw = wm == j ? f.b[j] : bw;
-          acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, f.ax, acc_x, 0, 0, 0);
-        }
-      }
-    }
   };
+  // tall tiles: the extra rows' MFMA of one k-step, after the stage's others
+  // (one branch per stage around both k-steps, none between the others)
+  auto mma_x = [&](const Frag& f) { acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.bx, f.ax, acc_x, 0, 0, 0); };
 
   // acc[j][i] holds output row 64 wm + 32 i + lane % 32, columns
   // col_base(j) + 8 q4 + 4 (lane / 32) + {0..3}
@@ -1020,9 +1018,17 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       if (active) {
         read_frag(slot_c, 0, f0);
         read_frag(slot_c, 1, f1);
+        if (TALL && cur_tall) {
+          read_x(slot_c, 0, f0);
+          read_x(slot_c, 1, f1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         mma(f0);
         mma(f1);
+        if (TALL && cur_tall) {
+          mma_x(f0);
+          mma_x(f1);
+        }
       }
     } else {
       // Ping-pong: waves 0-3 and waves 4-7 (one of each per SIMD) run the
@@ -1042,6 +1048,10 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       if (active) {
         read_frag(slot_c, 0, f0);
         read_frag(slot_c, 1, f1);
+        if (TALL && cur_tall) {
+          read_x(slot_c, 0, f0);
+          read_x(slot_c, 1, f1);
+        }
       }
       if (more) {
         // (tall tiles: waves 0 and 1 issue one load more per stage)
@@ -1057,6 +1067,10 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
         __builtin_amdgcn_s_setprio(1);
         mma(f0);
         mma(f1);
+        if (TALL && cur_tall) {
+          mma_x(f0);
+          mma_x(f1);
+        }
         __builtin_amdgcn_s_setprio(0);
       }
       barrier();
