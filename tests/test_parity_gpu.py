@@ -603,6 +603,55 @@ def test_forward_decode(tre):
     check_forward(tre, inp)
 
 
+def down_tile_plan(counts, max_rows, d, I, n_cus=256):
+    """The 256-row down projection's tiles for these expert row counts, as the
+    library plans them (tall last tiles, the split tail): names the paths a
+    test takes.  Returns (tall, tiles, grid, split tiles, pieces each)."""
+    E = len(counts)
+    big = max_rows >= 128 * E and I >= 96
+    if not big:
+        return False, 0, 0, 0, 1
+    tall = max_rows <= 384 * E
+    mt = [(c + 255) // 256 for c in counts]
+    if tall:
+        mt = [m - 1 if m > 1 and c - (m - 1) * 256 <= 32 else m for m, c in zip(mt, counts)]
+    nt = (d + 255) // 256
+    tiles = sum(mt) * nt
+    max_mt = max_rows // 256 + min(E, max_rows)
+    grid = min(max_mt * nt, n_cus)
+    grid = (grid + 7) // 8 * 8
+    exc, pieces = 0, 1
+    if max_mt * nt > n_cus and tiles > grid and tiles % grid:
+        e = tiles % grid
+        sp = min(4, grid // e, 256 // e, (I // 32) // 8)
+        if sp >= 2:
+            exc, pieces = e, sp
+    return tall, tiles, grid, exc, pieces
+
+
+@pytest.mark.parametrize("T,d,E,k,I,logits,want", [
+    (8192, 1024, 64, 2, 512, "normal", "tall+split"),    # ~256 rows an expert: tall tiles, a split tail
+    (6000, 768, 96, 4, 640, "uniform", "tall+split"),
+    (16000, 1024, 24, 1, 512, "normal_bias", "split"),  # one pair per token: the split tail writes the output rows
+    (12000, 512, 96, 2, 384, "normal", "tall"),
+])
+def test_forward_tall_and_split_tail_shapes(tre, T, d, E, k, I, logits, want):
+    # Layers whose down projection takes tall tiles and/or a split tail (the
+    # plan is recomputed here from the routing, to check the shape exercises
+    # what it is meant to): every token against the oracle, and the fused
+    # layer equal to grouping + grouped feed-forward + combine bit for bit.
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + E + I, logits=logits,
+                                name=f"tall_split_{T}_{E}")
+    idx, _ = oracle.route(inp.logits, k)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    tall, tiles, grid, exc, pieces = down_tile_plan(counts, T * k, d, I)
+    say(f"forward T={T} d={d} E={E} k={k} I={I}: down tall={tall} tiles={tiles} grid={grid} "
+        f"split {exc} tiles x {pieces}")
+    assert ("tall" in want) == tall and ("split" in want) == (exc > 0)
+    check_forward(tre, inp)
+    check_fused_equals_staged(tre, inp)
+
+
 @pytest.mark.parametrize("T,d,E,k,I,dtype,logits", [
     (1, 128, 16, 1, 128, "bf16", "normal"),          # a single token
     (5, 64, 256, 8, 64, "bf16", "normal"),           # most experts empty, widest E
