@@ -1034,6 +1034,7 @@ def test_backward_empty_batch(tre):
     (4096, 512, 8, 2, 576, "normal_bias"),   # 256-row tiles
     (600, 128, 16, 1, 128, None),            # given pairs, some masked
     (48, 256, 8, 2, 2048, "normal"),         # few rows: k-split down projection in both forwards
+    (16384, 1024, 64, 1, 512, "normal"),     # one pair per token, ~256 rows an expert: a split tail in both
 ])
 def test_training_step_saved_equals_recompute(tre, T, d, E, k, I, logits):
     # the training forward's output equals moe_forward's bit for bit, and the

@@ -432,8 +432,12 @@ moe_status forward_keep(const void* x, const float* logits, int32_t T, int32_t d
   TRY(from_hip(launch_move_rows(x, T, k, (int64_t)d * 2, p_row, P, x_perm, s)));
   TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up, h, gu, s, nullptr, 0,
                                         sched)));
-  return from_hip(
-      launch_down_bf16(h, offs, P, E, d, I, (const bf16_t*)w_down, y, s, (float*)(ws + L.split), sched));
+  // with one pair per token, moe_forward's down projection writes the output
+  // rows from its tiles; these rows come from the same tiles (so a split tail
+  // cuts the same ones and the output is moe_forward's bit for bit)
+  const bool scatter_tiles = k == 1 && down_scatters(P, E, d, I, true);
+  return from_hip(launch_down_bf16(h, offs, P, E, d, I, (const bf16_t*)w_down, y, s, (float*)(ws + L.split), sched,
+                                   nullptr, scatter_tiles));
 }
 
 }  // namespace

@@ -193,9 +193,12 @@ struct DownScatter {
   int64_t T;
 };
 bool down_scatters(int64_t max_rows, int E, int d, int I, bool have_split_ws);
+// scatter_tiles: grouped rows y, but in the tiles the scatter path (sc) would
+// use (no tall tiles), so that a split tail cuts the same tiles and the rows
+// equal, bit for bit, what the scatter path computes.
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws = nullptr,
-                            int32_t* sched = nullptr, const DownScatter* sc = nullptr);
+                            int32_t* sched = nullptr, const DownScatter* sc = nullptr, bool scatter_tiles = false);
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
                               int d, int I, const float* w_gate_up, float* h, hipStream_t s);
 hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,

@@ -1326,7 +1326,7 @@ template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
                        int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr,
-                       int32_t* sched = nullptr, float* tail_ws = nullptr);
+                       int32_t* sched = nullptr, float* tail_ws = nullptr, bool allow_tall = true);
 
 // 256-row tiles (8 waves in ping-pong, one workgroup per CU: each weight
 // stage feeds twice the rows) once the experts hold 128 rows or more on
@@ -1351,9 +1351,9 @@ bool tall_tiles(int64_t max_rows, int E) { return max_rows <= 384 * (int64_t)E; 
 template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token, int64_t a_rows,
-                       bf16_t* out2, const bf16_t* aux, int32_t* sched, float* tail_ws) {
+                       bf16_t* out2, const bf16_t* aux, int32_t* sched, float* tail_ws, bool allow_tall) {
   if constexpr (EPI == kEpiPlain && !BT) {
-    if (big_tiles(max_rows, E, K) && tall_tiles(max_rows, E) && row_token == nullptr)
+    if (allow_tall && big_tiles(max_rows, E, K) && tall_tiles(max_rows, E) && row_token == nullptr)
       return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, nullptr,
                                                              0, out2, aux, 1, tail_ws, sched);
   }
@@ -1414,7 +1414,7 @@ bool down_scatters(int64_t max_rows, int E, int d, int I, bool have_split_ws) {
 
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws,
-                            int32_t* sched, const DownScatter* sc) {
+                            int32_t* sched, const DownScatter* sc, bool scatter_tiles) {
   if (sc && !down_scatters(max_rows, E, d, I, split_ws != nullptr)) return hipErrorInvalidValue;
   {
     const bool small = small_tiles(max_rows, E);
@@ -1443,7 +1443,7 @@ hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int6
                                                               tail_ws, dn_sched, sc->row_w);
   else
     e = launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s, nullptr, 0,
-                                      nullptr, nullptr, dn_sched, tail_ws);
+                                      nullptr, nullptr, dn_sched, tail_ws, !scatter_tiles);
   if (e != hipSuccess || tail_ws == nullptr) return e;
   k_tail_sum<<<dim3(kTailPieces / 2, 288 / kTailSumRows), 256, 0, s>>>(
       tail_ws, d, sc ? sc->out : y_perm, sc ? sc->row_token : nullptr, sc ? sc->row_w : nullptr, sc ? sc->T : 0);
