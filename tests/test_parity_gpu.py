@@ -192,6 +192,12 @@ def check_permute(tre, x, pair_expert, k, E):
     (1024, 2, 256, 64, "bf16"),     # 2048 pairs: the largest one-workgroup grouping, two steps
     (2049, 1, 256, 64, "bf16"),     # 2049 pairs: the smallest chunked grouping
     (700, 3, 5, 64, "bf16"),        # one-workgroup grouping, ragged second step
+    (1500, 7, 33, 128, "bf16"),     # fused grouping + row move, one token a wave, pairs across chunk edges
+    (200, 20, 100, 64, "bf16"),     # 80 pairs a workgroup
+    (40, 70, 200, 64, "bf16"),      # more than 64 pairs a token: index kernels, then the row move
+    (1000, 3, 20, 8256, "bf16"),    # rows of three pieces (the last one 8 vectors)
+    (800, 4, 50, 4160, "f32"),      # float32 rows of three pieces
+    (70000, 4, 64, 64, "bf16"),     # 69 chunks of 4096 pairs: the one-workgroup scan before the fused kernel
 ])
 def test_permute_random(tre, T, k, E, d, dtype):
     rng = np.random.default_rng(T + k + E)
@@ -203,10 +209,11 @@ def test_permute_random(tre, T, k, E, d, dtype):
     check_permute(tre, inp.x, pe, k, E)
 
 
-def test_permute_out_of_range_ids_are_dropped(tre):
+@pytest.mark.parametrize("T", [700, 3000])   # one-workgroup grouping; fused grouping + row move
+def test_permute_out_of_range_ids_are_dropped(tre, T):
     rng = np.random.default_rng(3)
-    inp = workloads.make_custom(T=700, d=64, E=12, k=2, I=64, dtype="bf16", seed=3, weights=False)
-    pe = rng.integers(0, 12, size=1400).astype(np.int32)
+    inp = workloads.make_custom(T=T, d=64, E=12, k=2, I=64, dtype="bf16", seed=3, weights=False)
+    pe = rng.integers(0, 12, size=2 * T).astype(np.int32)
     pe[::5] = 12
     pe[1::7] = 1 << 20
     pe[2::11] = -9
@@ -657,6 +664,7 @@ def test_forward_tall_and_split_tail_shapes(tre, T, d, E, k, I, logits, want):
     (5, 64, 256, 8, 64, "bf16", "normal"),           # most experts empty, widest E
     (130, 128, 4, 4, 192, "bf16", "normal"),         # k = E
     (257, 64, 3, 2, 64, "f32", "uniform"),
+    (1500, 64, 6, 2, 128, "f32", "normal"),          # float32 layer past the one-workgroup grouping
     (1000, 192, 7, 3, 320, "bf16", "normal_bias"),
     (48, 256, 8, 2, 2048, "bf16", "normal"),         # few rows: k-split down projection
     (3, 64, 2, 1, 1024, "bf16", "normal"),           # a split over two ranges, one row per expert

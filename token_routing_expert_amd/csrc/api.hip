@@ -152,9 +152,10 @@ moe_status moe_permute(const void* x, moe_dtype dt, int32_t T, int32_t d, int32_
   if (workspace_bytes < moe_permute_workspace_size(T, k, E) || (T > 0 && !workspace)) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
-  TRY(from_hip(launch_permute_index(pair_expert, P, k, E, row_token, pair_row, expert_offsets, workspace, s)));
-  if (!x_perm) return MOE_OK;   // index only: the caller gathers rows itself
-  return from_hip(launch_move_rows(x, T, k, (int64_t)d * elem_size(dt), pair_row, P, x_perm, s));
+  if (!x_perm)   // index only: the caller gathers rows itself
+    return from_hip(launch_permute_index(pair_expert, P, k, E, row_token, pair_row, expert_offsets, workspace, s));
+  return from_hip(launch_permute_rows(pair_expert, T, k, E, row_token, pair_row, expert_offsets, workspace, s,
+                                      nullptr, x, (int64_t)d * elem_size(dt), x_perm));
 }
 
 size_t moe_grouped_ffn_workspace_size(int32_t max_rows, int32_t E, int32_t d, int32_t I, moe_dtype dt) {
@@ -307,9 +308,9 @@ moe_status forward_impl(const void* x, const float* logits, int32_t T, int32_t d
   // pass runs
   const bool scatter = dt == MOE_BF16 && k == 1 && down_scatters(P, E, d, I, true);
   float* row_w = scatter ? (float*)(ws + L.row_w) : nullptr;
-  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched,
-                                    scatter ? topk_w : nullptr, row_w)));
   if (dt == MOE_BF16) {
+    TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched,
+                                      scatter ? topk_w : nullptr, row_w)));
     if (scatter) TRY(from_hip(launch_zero_unrouted_bf16(p_row, P, T, d, (bf16_t*)out, s)));
     // the gate/up projection reads the token rows in place through row_token
     // (no expert-ordered copy of x is materialised)
@@ -324,7 +325,8 @@ moe_status forward_impl(const void* x, const float* logits, int32_t T, int32_t d
                                   (float*)(ws + L.split), sched)));
     return from_hip(launch_combine_bf16((const bf16_t*)y_perm, P, p_row, topk_w, T, k, d, (bf16_t*)out, s));
   }
-  TRY(from_hip(launch_move_rows(x, T, k, (int64_t)d * elem_size(dt), p_row, P, x_perm, s)));
+  TRY(from_hip(launch_permute_rows(topk_idx, T, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, nullptr, x,
+                                   (int64_t)d * elem_size(dt), x_perm)));
   TRY(from_hip(launch_grouped_ffn_f32((const float*)x_perm, offs, P, E, d, I, (const float*)w_gate_up,
                                       (const float*)w_down, (float*)h, (float*)y_perm, s)));
   return from_hip(launch_combine_f32((const float*)y_perm, P, p_row, topk_w, T, k, d, (float*)out, s));
@@ -428,8 +430,8 @@ moe_status forward_keep(const void* x, const float* logits, int32_t T, int32_t d
   bf16_t* y = (bf16_t*)(ws + L.y);
   if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
   int32_t* sched = (int32_t*)(ws + L.sched);
-  TRY(from_hip(launch_permute_index(topk_idx, P, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched)));
-  TRY(from_hip(launch_move_rows(x, T, k, (int64_t)d * 2, p_row, P, x_perm, s)));
+  TRY(from_hip(launch_permute_rows(topk_idx, T, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched, x,
+                                   (int64_t)d * 2, x_perm)));
   TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up, h, gu, s, nullptr, 0,
                                         sched)));
   // with one pair per token, moe_forward's down projection writes the output

@@ -159,6 +159,12 @@ hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, in
 // each row of x is read once); row_bytes % 16 == 0.
 hipError_t launch_move_rows(const void* x, int64_t T, int k, int64_t row_bytes, const int32_t* pair_row,
                             int64_t max_rows, void* x_perm, hipStream_t s);
+// The grouping (as launch_permute_index, without row weights) and the row move
+// (as launch_move_rows into P = T * k rows) together: for more than a
+// decode-sized batch, the scatter and the move are one kernel.
+hipError_t launch_permute_rows(const int32_t* pair_expert, int64_t T, int k, int E, int32_t* row_token,
+                               int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s, int32_t* sched,
+                               const void* x, int64_t row_bytes, void* x_perm);
 
 // Tile counters of the grouped products (zero before each product that uses
 // one): the gate/up product's at sched[0], the down product's at

@@ -24,8 +24,13 @@
 //            starting rows, which the scatter then reads.
 //   small    up to kSmallPairs pairs: one workgroup does all of the above in
 //            one launch.
-// The row move is a separate, bandwidth-bound kernel: one wave per
-// destination row, 16-byte vectors, rows written in order.
+//   rows     the scatter and the row move in one kernel (after hist): each
+//            workgroup places the pairs of a few tokens (summing the counts
+//            it needs itself) while its first row loads are in flight, then
+//            writes the tokens' rows to their grouped rows.
+// Without that fusion (decode-sized batches, more than 64 pairs a token) the
+// row move is its own bandwidth-bound kernel: one wave per token, its row read
+// once in 16-byte vectors and written to each of its grouped rows.
 #include "common.hpp"
 
 namespace tre {
@@ -34,15 +39,15 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void k_perm_hist(const int32_t* __restrict__ pair_expert, int64_t P,
-                                                        int E, int32_t* __restrict__ chunk_count,
+                                                        int E, int chunk_pairs, int32_t* __restrict__ chunk_count,
                                                         int32_t* __restrict__ sched) {
   __shared__ int cnt[kMaxExperts];
   const int tid = threadIdx.x;
   if (sched && blockIdx.x == 0 && tid < kSchedWords) sched[tid] = 0;
   if (tid < E) cnt[tid] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kPermuteChunk;
-  for (int i = tid; i < kPermuteChunk; i += kThreads) {
+  const int64_t base = (int64_t)blockIdx.x * chunk_pairs;
+  for (int i = tid; i < chunk_pairs; i += kThreads) {
     const int64_t p = base + i;
     if (p < P) {
       const int e = pair_expert[p];
@@ -331,6 +336,147 @@ __global__ __launch_bounds__(kThreads) void k_move_rows(const u32x4* __restrict_
   }
 }
 
+// The grouping and the row move in one launch, after k_perm_hist (and, for
+// many chunks, k_perm_scan).  A workgroup takes 4 * tpw consecutive tokens
+// (wave w: tokens w, w + 4, ...; at most kThreads pairs).  It first issues the
+// loads of each wave's first row piece, so that reading the rows overlaps the
+// index work.  It then places its own pairs where k_perm_scatter would: the
+// expert's offset, plus that expert's pairs in earlier chunks (the counts) and
+// in its own chunk before its first pair (counted here from the ids), plus the
+// rank among its own pairs (earlier waves' counts, the ballot rank within the
+// wave).  Last, every wave writes its tokens' row pieces to their grouped rows,
+// the next piece's loads issued before the current one is written.
+constexpr int kRowsWaves = kThreads / kWave;
+constexpr int kRowsVec = 8;   // 16-byte vectors a lane per row piece
+
+__global__ __launch_bounds__(kThreads) void k_perm_rows(
+    const int32_t* __restrict__ pair_expert, int64_t T, int k, int E, int chunk_pairs, int n_chunks,
+    const int32_t* __restrict__ chunk_count, const int32_t* __restrict__ chunk_base, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ pair_row, int32_t* __restrict__ row_token, const u32x4* __restrict__ x,
+    int64_t vec_per_row, int tpw, u32x4* __restrict__ x_perm) {
+  __shared__ int running[kMaxExperts];
+  __shared__ int s_before[kMaxExperts];
+  __shared__ int s_total[kMaxExperts];
+  __shared__ int wave_count[kRowsWaves][kMaxExperts];
+  __shared__ int s_wave[kRowsWaves];
+  __shared__ int s_row[kThreads];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int64_t P = T * k;
+  const int64_t t0 = (int64_t)blockIdx.x * (kRowsWaves * tpw);
+  const int n_tok = (int)min((int64_t)kRowsWaves * tpw, T - t0);
+  const int64_t p0 = t0 * k;
+  const int np = n_tok * k;
+  // work items of this wave: (token j, piece) for its tokens t0 + wave + 4 j
+  const int n_pieces = (int)ceil_div(vec_per_row, kRowsVec * kWave);
+  const int my_tok = n_tok > wave ? (n_tok - wave + kRowsWaves - 1) / kRowsWaves : 0;
+  const int items = my_tok * n_pieces;
+  u32x4 buf_a[kRowsVec], buf_b[kRowsVec];
+  auto load_item = [&](int i, u32x4(&buf)[kRowsVec]) {
+    const int j = i / n_pieces;
+    const u32x4* src = x + (t0 + wave + kRowsWaves * j) * vec_per_row;
+    const int64_t base = (int64_t)(i - j * n_pieces) * (kRowsVec * kWave);
+#pragma unroll
+    for (int u = 0; u < kRowsVec; ++u) {
+      const int64_t v = base + u * kWave + lane;
+      if (v < vec_per_row) buf[u] = src[v];
+    }
+  };
+  auto store_item = [&](int i, const u32x4(&buf)[kRowsVec]) {
+    const int j = i / n_pieces;
+    const int lt = wave + kRowsWaves * j;
+    const int64_t base = (int64_t)(i - j * n_pieces) * (kRowsVec * kWave);
+    for (int q = 0; q < k; ++q) {
+      const int r = s_row[lt * k + q];
+      if (r < 0 || r >= P) continue;
+      u32x4* dst = x_perm + (int64_t)r * vec_per_row;
+#pragma unroll
+      for (int u = 0; u < kRowsVec; ++u) {
+        const int64_t v = base + u * kWave + lane;
+        if (v < vec_per_row) dst[v] = buf[u];
+      }
+    }
+  };
+  if (items > 0) load_item(0, buf_a);
+  const int e = tid < np ? pair_expert[p0 + tid] : -1;
+  // each expert's pairs before this workgroup's first pair: in earlier chunks
+  // (with few experts, kThreads / E threads share an expert's chunks) ...
+  const int c0 = (int)(p0 / chunk_pairs);
+  if (tid < E) s_before[tid] = s_total[tid] = 0;
+  __syncthreads();
+  if (chunk_base) {
+    if (tid < E) atomicAdd(&s_before[tid], chunk_base[(int64_t)c0 * E + tid]);   // includes the expert's offset
+  } else {
+    const int parts = kThreads / E;
+    if (tid < parts * E) {
+      const int ex = tid % E;
+      int before = 0, total = 0;
+#pragma unroll 16
+      for (int b = tid / E; b < n_chunks; b += parts) {
+        const int v = chunk_count[(int64_t)b * E + ex];
+        total += v;
+        before += b < c0 ? v : 0;
+      }
+      atomicAdd(&s_total[ex], total);
+      atomicAdd(&s_before[ex], before);
+    }
+  }
+  // ... and in this chunk
+#pragma unroll 4
+  for (int64_t q = (int64_t)c0 * chunk_pairs + tid; q < p0; q += kThreads) {
+    const int eq = pair_expert[q];
+    if (eq >= 0 && eq < E) atomicAdd(&s_before[eq], 1);
+  }
+  __syncthreads();
+  if (chunk_base) {
+    if (tid < E) running[tid] = s_before[tid];
+  } else {
+    int all = 0;
+    const int start = block_exclusive_scan(tid < E ? s_total[tid] : 0, s_wave, &all);
+    if (tid < E) running[tid] = start + s_before[tid];
+    if (blockIdx.x == 0) {
+      if (tid < E) offsets[tid] = start;
+      if (tid == 0) offsets[E] = all;
+    }
+  }
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < kRowsWaves; ++w) wave_count[w][tid] = 0;
+  }
+  __syncthreads();
+  const bool valid = e >= 0 && e < E;
+  // lanes of this wave holding the same expert: eight ballots over the id bits
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool set = (e >> bit) & 1;
+    const uint64_t b = __ballot(set);
+    peers &= set ? b : ~b;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int rank = __popcll(peers & lt_mask);
+  if (valid && rank == 0) wave_count[wave][e] = __popcll(peers);
+  __syncthreads();
+  if (tid < np) {
+    int r = -1;
+    if (valid) {
+      r = running[e] + rank;
+      for (int w = 0; w < wave; ++w) r += wave_count[w][e];
+      if (r >= 0 && r < P) row_token[r] = (int32_t)(t0 + tid / k);
+    }
+    pair_row[p0 + tid] = r;
+    s_row[tid] = r;
+  }
+  __syncthreads();
+  for (int i = 0; i < items; i += 2) {
+    if (i + 1 < items) load_item(i + 1, buf_b);
+    store_item(i, buf_a);
+    if (i + 1 < items) {
+      if (i + 2 < items) load_item(i + 2, buf_a);
+      store_item(i + 1, buf_b);
+    }
+  }
+}
+
 }  // namespace
 
 // Chunk counts up to this many are summed by every scatter workgroup.
@@ -355,13 +501,48 @@ hipError_t launch_permute_index(const int32_t* pair_expert, int64_t P, int k, in
   const int n_chunks = (int)ceil_div(P, kPermuteChunk);
   int32_t* chunk_count = (int32_t*)ws;
   int32_t* chunk_base = nullptr;
-  k_perm_hist<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, E, chunk_count, sched);
+  k_perm_hist<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, E, kPermuteChunk, chunk_count, sched);
   if ((int64_t)n_chunks * E > kFusedScanMax) {
     chunk_base = chunk_count + (int64_t)n_chunks * E;
     k_perm_scan<<<1, kThreads, 0, s>>>(chunk_count, n_chunks, E, chunk_base, expert_offsets);
   }
   k_perm_scatter<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, k, E, n_chunks, chunk_count, chunk_base,
                                                expert_offsets, pair_row, row_token, pair_w, row_w);
+  return hipGetLastError();
+}
+
+// The grouping with its row move: k_perm_hist with chunks of up to
+// kRowsChunkMax pairs (at most kRowsChunks of them, else the one-workgroup
+// scan runs too), then k_perm_rows.  Small batches, and more than 64 pairs a
+// token, take the index kernels and k_move_rows.
+constexpr int kRowsChunks = 32;
+constexpr int kRowsChunkMax = 4096;
+
+hipError_t launch_permute_rows(const int32_t* pair_expert, int64_t T, int k, int E, int32_t* row_token,
+                               int32_t* pair_row, int32_t* expert_offsets, void* ws, hipStream_t s, int32_t* sched,
+                               const void* x, int64_t row_bytes, void* x_perm) {
+  const int64_t P = T * k;
+  if (P <= kSmallPairs || k > kThreads / kRowsWaves) {
+    const hipError_t err = launch_permute_index(pair_expert, P, k, E, row_token, pair_row, expert_offsets, ws, s,
+                                                sched);
+    if (err != hipSuccess) return err;
+    return launch_move_rows(x, T, k, row_bytes, pair_row, P, x_perm, s);
+  }
+  int64_t chunk = kPermuteChunk;
+  while (ceil_div(P, chunk) > kRowsChunks && chunk < kRowsChunkMax) chunk *= 2;
+  const int n_chunks = (int)ceil_div(P, chunk);   // <= ceil(P / kPermuteChunk): fits the workspace
+  int32_t* chunk_count = (int32_t*)ws;
+  int32_t* chunk_base = nullptr;
+  k_perm_hist<<<n_chunks, kThreads, 0, s>>>(pair_expert, P, E, (int)chunk, chunk_count, sched);
+  if (n_chunks > kRowsChunks) {
+    chunk_base = chunk_count + (int64_t)n_chunks * E;
+    k_perm_scan<<<1, kThreads, 0, s>>>(chunk_count, n_chunks, E, chunk_base, expert_offsets);
+  }
+  const int tpw = k >= 8 ? 1 : 8 / k;
+  const int64_t blocks = ceil_div(T, kRowsWaves * tpw);
+  k_perm_rows<<<(unsigned)blocks, kThreads, 0, s>>>(pair_expert, T, k, E, (int)chunk, n_chunks, chunk_count,
+                                                    chunk_base, expert_offsets, pair_row, row_token,
+                                                    (const u32x4*)x, row_bytes / 16, tpw, (u32x4*)x_perm);
   return hipGetLastError();
 }
 
