@@ -987,6 +987,7 @@ def check_backward(tre, inp, seed):
     (64, 128, 16, 1, 128, "normal"),         # k = 1: no logit gradient
     (5, 64, 256, 8, 64, "normal"),           # most experts empty, widest E
     (4096, 512, 8, 2, 576, "normal_bias"),   # 256-row tiles, I not a multiple of 128
+    (2000, 128, 1, 1, 192, "normal"),        # one expert: its weight-gradient tiles shared out over the XCDs
 ])
 def test_backward_shapes(tre, T, d, E, k, I, logits):
     inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + E + 50, logits=logits)
