@@ -386,6 +386,9 @@ def main() -> int:
                     help="MiB of scratch read before every timed step (0: no flush)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the router projection, permute-with-rows, graph and backward measurements")
+    ap.add_argument("--extras", default="graph,permute,router,backward",
+                    help="comma-separated measurements beside the layer (graph, permute, router, backward); "
+                         "--no-extras is the same as none")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -436,26 +439,28 @@ def main() -> int:
     roofline = roofline_of(inp, kernels, work, peak_mm, args.workload)
 
     graph_ms = permute_rows = router = backward = None
-    if not args.no_extras:
-        # ---- timed region 3: the same layer captured once as a HIP graph and
-        # replayed K times back to back (what a decode loop would do; the
-        # library records no host work, so the whole layer is one graph) ----
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cap):
-            layer.fused(stream=cap)
-        for _ in range(args.warmup):
-            graph.replay()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        g0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / args.steps
-        del graph
+    extras = set() if args.no_extras else {e for e in args.extras.split(",") if e and e != "none"}
+    if extras:
+        if "graph" in extras:
+            # ---- timed region 3: the same layer captured once as a HIP graph and
+            # replayed K times back to back (what a decode loop would do; the
+            # library records no host work, so the whole layer is one graph) ----
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=cap):
+                layer.fused(stream=cap)
+            for _ in range(args.warmup):
+                graph.replay()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            g0.record(stream)
+            for _ in range(args.steps):
+                graph.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            graph_ms = g0.elapsed_time(g1) / args.steps
+            del graph
 
         def timed_cold(fn, n):
             # n cold calls: flush, event, call, event
@@ -469,35 +474,36 @@ def main() -> int:
             torch.cuda.synchronize()
             return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
 
-        # ---- timed region 4: the permutation with its row moves (moe_permute
-        # with x_perm), the step as the benchmark defines it: each token row
-        # read once and written to its k grouped rows, plus the index arrays.
-        # The fused bf16 layer skips the row copy (its gate/up reads token rows
-        # in place), so this is reported beside the layer.
-        xp_rows = torch.empty((P, d), dtype=dev_dtype, device="cuda")
-        pr_tok = torch.empty(P, dtype=torch.int32, device="cuda")
-        pr_row = torch.empty(P, dtype=torch.int32, device="cuda")
-        pr_off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        if "permute" in extras:
+            # ---- timed region 4: the permutation with its row moves (moe_permute
+            # with x_perm), the step as the benchmark defines it: each token row
+            # read once and written to its k grouped rows, plus the index arrays.
+            # The fused bf16 layer skips the row copy (its gate/up reads token rows
+            # in place), so this is reported beside the layer.
+            xp_rows = torch.empty((P, d), dtype=dev_dtype, device="cuda")
+            pr_tok = torch.empty(P, dtype=torch.int32, device="cuda")
+            pr_row = torch.empty(P, dtype=torch.int32, device="cuda")
+            pr_off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
 
-        def run_permute_rows():
-            st = lib.moe_permute(ptr(x), dt, T, d, k, ptr(topk_idx), E, ptr(xp_rows), ptr(pr_tok), ptr(pr_row),
-                                 ptr(pr_off), ptr(layer.pws), layer.pws_bytes, sp)
-            if st != 0:
-                raise RuntimeError(f"moe_permute failed with status {st}")
-        for _ in range(args.warmup):
-            run_permute_rows()
-        pr_ms = timed_cold(run_permute_rows, args.steps)
-        s_elem = 4 if inp.dtype == "f32" else 2
-        pr_bytes = T * d * s_elem * (1 + k) + 16 * P
-        permute_rows = {"ms": round(pr_ms, 5), "bytes_per_call": pr_bytes,
-                        "gbs": round(pr_bytes / (pr_ms * 1e-3) / 1e9, 1),
-                        "hbm_frac": round(pr_bytes / (pr_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        del xp_rows
+            def run_permute_rows():
+                st = lib.moe_permute(ptr(x), dt, T, d, k, ptr(topk_idx), E, ptr(xp_rows), ptr(pr_tok), ptr(pr_row),
+                                     ptr(pr_off), ptr(layer.pws), layer.pws_bytes, sp)
+                if st != 0:
+                    raise RuntimeError(f"moe_permute failed with status {st}")
+            for _ in range(args.warmup):
+                run_permute_rows()
+            pr_ms = timed_cold(run_permute_rows, args.steps)
+            s_elem = 4 if inp.dtype == "f32" else 2
+            pr_bytes = T * d * s_elem * (1 + k) + 16 * P
+            permute_rows = {"ms": round(pr_ms, 5), "bytes_per_call": pr_bytes,
+                            "gbs": round(pr_bytes / (pr_ms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(pr_bytes / (pr_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del xp_rows
 
         # ---- timed region 5 (beside the layer, not part of it): the router
         # projection fused with routing, x @ W_r^T then top-k, on the
         # workload's tokens and a seeded router weight [E, d] ----
-        if logits is not None:
+        if "router" in extras and logits is not None:
             w_r = to_device(workloads.router_weight(inp), torch)
             r_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
             r_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
@@ -521,7 +527,7 @@ def main() -> int:
         # moe_backward, which recomputes the forward it needs, and a training
         # step (the forward that keeps its intermediates, then the backward
         # from them) ----
-        if inp.dtype == "bf16":
+        if "backward" in extras and inp.dtype == "bf16":
             rng = np.random.default_rng([inp_seed(args.workload), 99])
             dout = to_device(workloads.bf16_bits(rng.normal(size=(T, d)).astype(np.float32)), torch)
             gdx = torch.empty((T, d), dtype=dev_dtype, device="cuda")
