@@ -129,20 +129,20 @@ __global__ __launch_bounds__(kThreads) void k_perm_scatter(const int32_t* __rest
   } else {
     if (tid < E) s_before[tid] = s_total[tid] = 0;
     __syncthreads();
-    // all threads read the counts together, four loads in flight each
-    const int n = n_chunks * E;
-    for (int i0 = tid; i0 < n; i0 += 4 * kThreads) {
-      int c[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) c[u] = (i0 + u * kThreads < n) ? chunk_count[i0 + u * kThreads] : 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kThreads;
-        if (c[u] != 0) {
-          atomicAdd(&s_total[i % E], c[u]);
-          if (i / E < chunk) atomicAdd(&s_before[i % E], c[u]);
-        }
+    // kThreads / E threads share an expert's chunks, all of a thread's loads
+    // in flight together
+    const int parts = kThreads / E;
+    if (tid < parts * E) {
+      const int ex = tid % E;
+      int before = 0, total = 0;
+#pragma unroll 16
+      for (int b = tid / E; b < n_chunks; b += parts) {
+        const int v = chunk_count[(int64_t)b * E + ex];
+        total += v;
+        before += b < chunk ? v : 0;
       }
+      atomicAdd(&s_total[ex], total);
+      atomicAdd(&s_before[ex], before);
     }
     __syncthreads();
     const int total = tid < E ? s_total[tid] : 0;
