@@ -219,6 +219,22 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
                 "tall tiles: ping-pong plain or gate/up products only");
   constexpr int XR = TALL ? 32 : 0;
   constexpr int A_STAGE = GE::A_BYTES + XR * BK * 2;  // LDS bytes of an activation stage
+  typedef Geo<2 * BK, NJ, WM> GD;  // the activation geometry of a double-stage
+  // Activation double-stages (the ping-pong products with [K][N] weights):
+  // the activation rows of two consecutive k-stages arrive together, 128
+  // bytes of a row per load lane group (8 rows per DMA instruction), in a
+  // ring of two double-stages beside the four-stage weight ring.  A load
+  // then asks L2 for whole 128-byte lines instead of half lines: half the
+  // requests for the same bytes, and the number of requests a CU can have
+  // in flight is what paces these loads.  The activation loads of stages
+  // g, g + 1 (g even) are issued with the weight loads of stage g + 1.
+  constexpr bool AD = PP && !BT;
+  static_assert(!AD || (BK == 32 && NS == 4 && WAVES == 8), "double-stages: 32-wide stages, a ring of four");
+  constexpr int AD_ROW = 4 * BK;                    // bytes of a row in a double-stage
+  constexpr int A_DSTAGE = (BM + XR) * AD_ROW;      // LDS bytes of a double-stage
+  constexpr int A_INSTR_D = BM * AD_ROW / 1024 / WAVES;  // activation loads per wave and double-stage
+  constexpr int XR_WAVES = XR * AD_ROW / 1024;      // waves with one load of the extra rows
+  static_assert(!AD || 2 * A_DSTAGE <= NS * A_STAGE, "the double-stage ring fits the stage ring's LDS");
   __shared__ __attribute__((aligned(1024))) char sA[NS * A_STAGE];
   __shared__ __attribute__((aligned(1024))) char sB[NS * GE::B_BYTES];
   // (tall tiles: the index of rows BM .. BM + XR - 1 arrives by a second
@@ -298,9 +314,10 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   };
   auto unit_range = [&](int64_t u, int& k0, int& k1) {
     if (TAIL && tS > 1 && u >= t_full) {
+      // (whole double-stages: every piece starts at an even stage)
       const int pc = (int)(u - t_full) % tS;
-      k0 = pc * nk / tS;
-      k1 = (pc + 1) * nk / tS;
+      k0 = AD ? 2 * (pc * (nk / 2) / tS) : pc * nk / tS;
+      k1 = AD ? 2 * ((pc + 1) * (nk / 2) / tS) : (pc + 1) * nk / tS;
       return pc;
     }
     const int sp = (int)(u % n_split);
@@ -414,8 +431,10 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   };
   __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferConfig);
   __amdgpu_buffer_rsrc_t b_rsrc = a_rsrc;
-  uint32_t a_voff[GE::A_INSTR], b_voff[GE::B_INSTR];
-  uint32_t ax_voff = kOutOfRange;  // tall tiles: this lane's chunk of the extra rows (waves 0, 1)
+  uint32_t a_voff[AD ? A_INSTR_D : GE::A_INSTR], b_voff[GE::B_INSTR];
+  // tall tiles: this lane's chunk of the extra rows (waves 0, 1; with
+  // double-stages waves 0 .. 3)
+  uint32_t ax_voff = kOutOfRange;
   // byte offsets of the next stage's k-columns in the activation and weight
   // buffers: scalar, added to every lane's offset by the load itself
   uint32_t ka = 0, kb = 0;
@@ -471,10 +490,14 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     const int64_t w_elems = BT ? (int64_t)N * K : (int64_t)K * ldw;
     b_rsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(W + (int64_t)t.e * w_elems), (short)0,
                                                __builtin_amdgcn_readfirstlane((int)(w_elems * 2)), kBufferConfig);
+    // (double-stages: instruction p of this wave fills rows (wave + WAVES p)
+    // 8 + lane / 8 with 64 k-values each, chunk lane % 8 of the LDS row)
+    constexpr int ARPI = AD ? GD::RPI : GE::RPI, ACPR = AD ? GD::CPR : GE::CPR;
+    auto aswz = [](int r) { return AD ? GD::swz(r) : GE::swz(r); };
 #pragma unroll
-    for (int p = 0; p < GE::A_INSTR; ++p) {
-      const int r = (wave + WAVES * p) * GE::RPI + lane / GE::CPR;
-      const int c = (lane % GE::CPR) ^ GE::swz(r);
+    for (int p = 0; p < (AD ? A_INSTR_D : GE::A_INSTR); ++p) {
+      const int r = (wave + WAVES * p) * ARPI + lane / ACPR;
+      const int c = (lane % ACPR) ^ aswz(r);
       int64_t src = r;
       if (gather) src = (r < t.rows) ? s_rt[slot][r] : -1;
       a_voff[p] = (r < t.rows && src >= 0 && src < (gather ? a_rows : (int64_t)t.rows))
@@ -482,12 +505,14 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
                       : kOutOfRange;
     }
     if constexpr (TALL) {
-      // rows BM + 16 wave .. + 15 of the tile, the A buffer spans t.rows rows
-      const int r = BM + 16 * wave + lane / GE::CPR;
-      const int c = (lane % GE::CPR) ^ GE::swz(r);
+      // rows BM + ARPI wave .. of the tile (waves 0 .. XW - 1), the A buffer
+      // spans t.rows rows
+      constexpr int XW = AD ? XR_WAVES : 2;
+      const int r = BM + ARPI * wave + lane / ACPR;
+      const int c = (lane % ACPR) ^ aswz(r);
       int64_t src = r;
-      if (gather) src = (wave < 2 && r < t.rows) ? s_rt[slot][r] : -1;
-      ax_voff = (wave < 2 && r < t.rows && src >= 0 && src < (gather ? a_rows : (int64_t)t.rows))
+      if (gather) src = (wave < XW && r < t.rows) ? s_rt[slot][r] : -1;
+      ax_voff = (wave < XW && r < t.rows && src >= 0 && src < (gather ? a_rows : (int64_t)t.rows))
                     ? (uint32_t)(src * K + c * 8) * 2u
                     : kOutOfRange;
     }
@@ -540,13 +565,29 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   auto issue = [&](auto slot_c) {
     constexpr int SLOT = decltype(slot_c)::value;
     if (i_k == 0) enter();
+    if constexpr (AD) {
+      // an odd stage of the stream (every tile has an even number of stages
+      // and starts at an even one): the activations of this stage and the
+      // one before, into double-stage slot SLOT / 2, ahead of the weights
+      if constexpr (SLOT % 2 == 1) {
+        constexpr int DOFF = (SLOT / 2) * A_DSTAGE;
 #pragma unroll
-    for (int p = 0; p < GE::A_INSTR; ++p)
-      dma16s(a_rsrc, a_lds0 + SLOT * A_STAGE + p * WAVES * 1024, a_voff[p], ka);
-    // in every stage, tall tile or not, so that waves 0 and 1 always count
-    // exactly one load more per stage (past the tile's rows it fetches nothing)
-    if constexpr (TALL)
-      if (wave < 2) dma16s(a_rsrc, a_lds0 + SLOT * A_STAGE + GE::A_BYTES, ax_voff, ka);
+        for (int p = 0; p < A_INSTR_D; ++p)
+          dma16s(a_rsrc, a_lds0 + DOFF + p * WAVES * 1024, a_voff[p], ka - kAStep);
+        // in every double-stage, tall tile or not, so that waves 0 .. 3
+        // always count exactly one load more
+        if constexpr (TALL)
+          if (wave < XR_WAVES) dma16s(a_rsrc, a_lds0 + DOFF + BM * AD_ROW, ax_voff, ka - kAStep);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < GE::A_INSTR; ++p)
+        dma16s(a_rsrc, a_lds0 + SLOT * A_STAGE + p * WAVES * 1024, a_voff[p], ka);
+      // in every stage, tall tile or not, so that waves 0 and 1 always count
+      // exactly one load more per stage (past the tile's rows it fetches nothing)
+      if constexpr (TALL)
+        if (wave < 2) dma16s(a_rsrc, a_lds0 + SLOT * A_STAGE + GE::A_BYTES, ax_voff, ka);
+    }
 #pragma unroll
     for (int p = 0; p < GE::B_INSTR; ++p)
       dma16s(b_rsrc, b_lds0 + SLOT * GE::B_BYTES + p * WAVES * 1024, b_voff[p], kb);
@@ -591,10 +632,14 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   uint32_t fa[2], fb[NFB], fax[2] = {0u, 0u}, fbx = 0u;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    fa[ks] = lds_address(sA) + GE::a_byte(64 * wm + lane % 32, ks * 2 + lane / 32);
+    // (double-stages: the even stage's chunks; the odd stage's chunk c + 4
+    // of a row sits at the address XOR 64, see read_frag)
+    fa[ks] = lds_address(sA) + (AD ? GD::a_byte(64 * wm + lane % 32, ks * 2 + lane / 32)
+                                   : GE::a_byte(64 * wm + lane % 32, ks * 2 + lane / 32));
     asm("" : "+v"(fa[ks]));
     if constexpr (TALL) {
-      fax[ks] = lds_address(sA) + GE::a_byte(BM + lane % 32, ks * 2 + lane / 32);
+      fax[ks] = lds_address(sA) + (AD ? GD::a_byte(BM + lane % 32, ks * 2 + lane / 32)
+                                      : GE::a_byte(BM + lane % 32, ks * 2 + lane / 32));
       asm("" : "+v"(fax[ks]));
     }
   }
@@ -631,12 +676,29 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * GE::BROW));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  // The activation fragment base of ring slot SLOT.  With double-stages,
+  // an odd stage reads chunk c + 4 = c ^ 4 of the rows the even stage reads
+  // at chunk c (c < 4), which the swizzle puts at the even stage's address
+  // XOR 64 (every other offset added to a base is a multiple of 128); the
+  // XOR is issued at each use, so that no second set of bases stays live.
+  auto a_base = [&](auto slot_c, uint32_t base) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    if constexpr (AD && SLOT % 2 == 1) asm volatile("v_xor_b32 %0, 64, %0" : "+v"(base));
+    return base;
+  };
+  // LDS offset of ring slot SLOT's activations, and of the second 32-row block
+  auto a_off = [&](auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    return AD ? (SLOT / 2) * A_DSTAGE : SLOT * A_STAGE;
+  };
+  constexpr int A_BLK32 = 32 * (AD ? AD_ROW : BK * 2);
   // the stage in ring slot SLOT, k-step ks
   auto read_frag = [&](auto slot_c, int ks, Frag& f) {
     constexpr int SLOT = decltype(slot_c)::value;
-    constexpr int A_OFF = SLOT * A_STAGE, B_OFF = SLOT * GE::B_BYTES;
+    constexpr int B_OFF = SLOT * GE::B_BYTES;
+    const uint32_t ab = a_base(slot_c, fa[ks]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f.a[i] = read_a(fa[ks], A_OFF + i * 32 * BK * 2);
+    for (int i = 0; i < 2; ++i) f.a[i] = read_a(ab, a_off(slot_c) + i * A_BLK32);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if constexpr (BT) {
@@ -653,7 +715,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   // block, read a second time), after the stage's other reads
   auto read_x = [&](auto slot_c, int ks, Frag& f) {
     constexpr int SLOT = decltype(slot_c)::value;
-    f.ax = read_a(fax[ks], SLOT * A_STAGE);
+    f.ax = read_a(a_base(slot_c, fax[ks]), a_off(slot_c));
     f.bx = read_b(fbx, SLOT * GE::B_BYTES + ks * 16 * GE::BROW);
   };
   auto mma = [&](const Frag& f) {
@@ -1053,7 +1115,23 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
           read_x(slot_c, 1, f1);
         }
       }
-      if (more) {
+      if constexpr (AD) {
+        // Double-stages: stage g + 1 is the weights issued two phases ago and
+        // the activations issued with them (g even) or in the last phase (g
+        // odd).  Issued since: g even -- the last phase's weights, this
+        // phase's activations and weights; g odd -- the last phase's weights
+        // and this phase's.  (Tall tiles: waves 0 .. 3 load one more
+        // activation instruction per double-stage.)
+        constexpr int NW = GE::B_INSTR;
+        if (!more) {
+          wait_vmcnt<0>();
+        } else if constexpr (SLOT % 2 == 0) {
+          if (TALL && wave < XR_WAVES) wait_vmcnt<2 * NW + A_INSTR_D + 1>();
+          else wait_vmcnt<2 * NW + A_INSTR_D>();
+        } else {
+          wait_vmcnt<2 * NW>();
+        }
+      } else if (more) {
         // (tall tiles: waves 0 and 1 issue one load more per stage)
         if (TALL && wave < 2) wait_vmcnt<(NS - 2) * (GE::PER_STAGE + 1)>();
         else wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
@@ -1080,8 +1158,13 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   };
 
   if constexpr (PP) {
-    // waves 4-7 start one barrier behind (see the stage body)
-    wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
+    // waves 4-7 start one barrier behind (see the stage body).  Stage 0 has
+    // landed once at most the loads of stages 1 and 2 are outstanding (with
+    // double-stages: the weights of stages 1 and 2, issued after stage 0's
+    // activations).
+    if (AD && 2 < total) wait_vmcnt<2 * GE::B_INSTR>();
+    else if (AD) wait_vmcnt<0>();
+    else wait_vmcnt<(NS - 2) * GE::PER_STAGE>();
     barrier();
     if (wave >= 4) barrier();
   }
