@@ -60,6 +60,8 @@ struct Vec<float> {
 // Up to KS slots: each lane first loads its vector of every slot's row (a
 // row index clamped into range, a dropped slot's value discarded by a
 // select), for two vectors at a time, so 2 KS gathers are in flight together.
+// Every expert row is read once: non-temporal loads (measured: the cold
+// combine of the 128-expert layer 47.5 -> 45.3 us).
 template <typename Elem, int KS>
 __device__ __forceinline__ void combine_token(const u32x4* __restrict__ y, int64_t max_rows,
                                               const int32_t* __restrict__ pair_row, const float* __restrict__ pair_w,
@@ -83,7 +85,7 @@ __device__ __forceinline__ void combine_token(const u32x4* __restrict__ y, int64
       const int64_t v = v0 + h * kWave;
 #pragma unroll
       for (int j = 0; j < KS; ++j)
-        if (j < k && max_rows > 0 && v < vec_per_row) g[h][j] = y[row[j] * vec_per_row + v];
+        if (j < k && max_rows > 0 && v < vec_per_row) g[h][j] = __builtin_nontemporal_load(&y[row[j] * vec_per_row + v]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

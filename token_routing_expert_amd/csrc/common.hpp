@@ -95,6 +95,17 @@ __device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds
                : "memory");
 }
 
+// The same load marked non-temporal (the nt cache policy): for a stream
+// read once, so that it does not push data that will be read again out of
+// L2.
+__device__ __forceinline__ void dma16s_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, uint32_t voffset,
+                                          uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "memory");
+}
+
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));

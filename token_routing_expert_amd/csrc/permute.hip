@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void k_move_rows(const u32x4* __restrict_
 #pragma unroll
     for (int i = 0; i < kMoveVec; ++i) {
       const int64_t v = base + i * kWave + lane;
-      if (v < vec_per_row) piece[i] = src[v];
+      if (v < vec_per_row) piece[i] = __builtin_nontemporal_load(&src[v]);   // each token row is read once
     }
     for (int j = 0; j < k; ++j) {
       const int64_t r = pair_row[t * k + j];
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void k_perm_rows(
 #pragma unroll
     for (int u = 0; u < kRowsVec; ++u) {
       const int64_t v = base + u * kWave + lane;
-      if (v < vec_per_row) buf[u] = src[v];
+      if (v < vec_per_row) buf[u] = __builtin_nontemporal_load(&src[v]);   // each token row is read once
     }
   };
   auto store_item = [&](int i, const u32x4(&buf)[kRowsVec]) {
