@@ -46,6 +46,11 @@ def row_rel_l2(got, ref) -> np.ndarray:
     return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
 
 
+# (label, whole-tensor rel-L2, worst row rel-L2, worst row, rows) of every
+# labelled check in this session, printed at the end of the run
+PARITY_LOG = []
+
+
 def check_outputs(got, ref, tol, label=""):
     """Whole-tensor relative L2 within tol AND every row within tol on its
     own: a single wrong or unwritten row (which adds only about 1/sqrt(rows)
@@ -58,6 +63,7 @@ def check_outputs(got, ref, tol, label=""):
     if label:
         print(f"  {label}: out rel_l2={whole:.3e}, worst row {worst} rel_l2={w:.3e} over {rows.size} rows",
               flush=True)
+        PARITY_LOG.append((label, whole, w, worst, int(rows.size), tol))
     assert not np.any(np.isnan(as_f64(np.asarray(got)))), f"{label}: NaN in the output"
     assert whole <= tol, f"{label}: whole-tensor rel_l2 {whole:.3e} > {tol}"
     assert w <= tol, f"{label}: row {worst} rel_l2 {w:.3e} > {tol}"
