@@ -1,16 +1,15 @@
-"""The grouped GEMM's tile claim, checked in the gfx950 assembly the compiler
-writes for it.
+"""The grouped GEMM's tile claim and register use, checked in the gfx950
+assembly the compiler writes for it.
 
-A claiming wave issues its atomic fetch-add in inline assembly and copies the
-returned ticket into LDS, again in inline assembly, a few stages later.  In
-between, the return is still in flight (nothing waits on it until the stage
-waits cover it), so no other instruction may read or write the ticket's
-register there.  The compiler does not know the register is busy, so this
-test compiles the kernel source and checks, for every kernel that claims,
-that the register's only references are the atomic and the LDS store.
+One lane of wave 0 claims a tile with an atomic fetch-add the compiler sees
+(not inline assembly), so the compiler keeps the returned value's register
+reserved until the return has landed.  The stage loads, however, are inline
+assembly that the compiler does not count: before the ticket is first used,
+only a full wait (vmcnt(0)) proves the return has arrived.  This test
+compiles the kernel source and checks, for every kernel that claims, that
+the compiler put one there; and that no instance of the grouped GEMM spills.
 Runs on the CPU (hipcc cross-compiles).  Without hipcc the library cannot be
-built either, so a missing hipcc fails the test instead of skipping it: the
-check must not go quiet while the kernels keep running."""
+built either, so a missing hipcc fails the test instead of skipping it."""
 import os
 import re
 import shutil
@@ -21,48 +20,57 @@ import pytest
 from token_routing_expert_amd import build as tre_build
 
 GEMM = re.compile(r"^(_ZN3tre\S*k_grouped_gemm\S*):")
-CLAIM = re.compile(r"global_atomic_add (v\d+), v\[\d+:\d+\], v\d+, off sc0")
+CLAIM = re.compile(r"global_atomic_add(?:_u32)? (v\d+), .* sc0")
 VREF = re.compile(r"\bv(\d+)\b|v\[(\d+):(\d+)\]")
 
 
-def ticket_references(asm: str):
-    """{kernel: (ticket registers, [other instructions naming one of them])}"""
+def claims_without_wait(asm: str):
+    """{kernel: number of claims} and [(kernel, first use) of a ticket read
+    with no vmcnt(0) between the claim and that use]"""
     lines = asm.split("\n")
     starts = [(i, m.group(1)) for i, l in enumerate(lines) if (m := GEMM.match(l))]
-    out = {}
+    counts, bad = {}, []
     for j, (a, name) in enumerate(starts):
         b = starts[j + 1][0] if j + 1 < len(starts) else len(lines)
         body = [l.split(";")[0].strip() for l in lines[a + 1:b]]
-        regs = {int(m.group(1)[1:]) for l in body if (m := CLAIM.search(l))}
-        other = []
-        for n in regs:
-            for ins in body:
-                if not ins or ins.startswith(".") or ins.endswith(":"):
-                    continue
-                named = any((m.group(1) and int(m.group(1)) == n) or
-                            (m.group(2) and int(m.group(2)) <= n <= int(m.group(3))) for m in VREF.finditer(ins))
-                if not named or CLAIM.search(ins) or re.fullmatch(r"ds_write_b32 v\d+, v%d" % n, ins):
-                    continue
-                other.append(ins)
-        out[name] = (regs, other)
-    return out
+        for i, ins in enumerate(body):
+            m = CLAIM.search(ins)
+            if not m:
+                continue
+            counts[name] = counts.get(name, 0) + 1
+            n = int(m.group(1)[1:])
+            waited = False
+            for later in body[i + 1:]:
+                if later.startswith("s_waitcnt") and "vmcnt(0)" in later:
+                    waited = True
+                if any((r.group(1) and int(r.group(1)) == n) or
+                       (r.group(2) and int(r.group(2)) <= n <= int(r.group(3))) for r in VREF.finditer(later)):
+                    if not waited:
+                        bad.append((name, later))
+                    break
+    return counts, bad
 
 
-def test_checker_sees_a_planted_reference():
+def test_checker_sees_a_missing_wait():
     asm = "\n".join([
         "_ZN3tre12_GLOBAL__N_13dma14k_grouped_gemmILi1EEEv:",
-        "  global_atomic_add v208, v[2:3], v12, off sc0",
-        "  v_add_u32_e32 v1, v208, v2",
-        "  ds_write_b32 v3, v208",
+        "  global_atomic_add v8, v1, v2, s[4:5] sc0",
+        "  s_waitcnt vmcnt(2)",
+        "  v_readfirstlane_b32 s3, v8",
+        "_ZN3tre12_GLOBAL__N_13dma14k_grouped_gemmILi2EEEv:",
+        "  global_atomic_add v8, v1, v2, s[4:5] sc0",
+        "  s_waitcnt vmcnt(0)",
+        "  v_readfirstlane_b32 s3, v8",
     ])
-    regs, other = ticket_references(asm)["_ZN3tre12_GLOBAL__N_13dma14k_grouped_gemmILi1EEEv"]
-    assert regs == {208} and other == ["v_add_u32_e32 v1, v208, v2"]
+    counts, bad = claims_without_wait(asm)
+    assert len(counts) == 2
+    assert bad == [("_ZN3tre12_GLOBAL__N_13dma14k_grouped_gemmILi1EEEv", "v_readfirstlane_b32 s3, v8")]
 
 
 @pytest.fixture(scope="module")
 def gemm_asm(tmp_path_factory):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    assert os.path.exists(hipcc), "hipcc not found: the claim check needs the kernels' gfx950 assembly"
+    assert os.path.exists(hipcc), "hipcc not found: the checks need the kernels' gfx950 assembly"
     src = os.path.join(tre_build.CSRC, "grouped_ffn.hip")
     out = tmp_path_factory.mktemp("asm") / "grouped_ffn.s"
     r = subprocess.run([hipcc, *tre_build.FLAGS, "--cuda-device-only", "-S", src, "-o", str(out)],
@@ -72,12 +80,10 @@ def gemm_asm(tmp_path_factory):
 
 
 @pytest.mark.timeout(600)
-def test_ticket_register_untouched_between_claim_and_post(gemm_asm):
-    refs = ticket_references(gemm_asm)
-    claiming = {k: v for k, v in refs.items() if v[0]}
-    assert claiming, "no kernel claims tiles: the claim's instruction pattern changed"
-    for name, (regs, other) in claiming.items():
-        assert not other, f"{name}: ticket register v{sorted(regs)} also used by {other[:4]}"
+def test_ticket_read_only_after_a_full_wait(gemm_asm):
+    counts, bad = claims_without_wait(gemm_asm)
+    assert counts, "no kernel claims tiles: the claim's instruction pattern changed"
+    assert not bad, f"a ticket is read before its return is waited for: {bad[:3]}"
 
 
 @pytest.mark.timeout(600)

@@ -28,6 +28,8 @@
 //     ring slots and LDS addresses are constants and a stage costs four
 //     loads, the LDS reads and the MFMAs plus a handful of scalar
 //     instructions;
+//   * in the 256-row (ping-pong) products the activation rows of two
+//     consecutive k-stages load together, whole 128-byte lines per row;
 //   * the gate/up activation loads gather token rows through row_token (the
 //     index of each tile is itself fetched into LDS by DMA a tile ahead);
 //   * weight rows are n-contiguous and reach the MFMA through the gfx950
@@ -393,41 +395,27 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   Tile inext = decode(unit_tile(vb), i_cursor);  // the tile the issue side enters next
   int64_t inext_u = vb;                           // and its unit
   int total = total_stages;  // stages of the tiles known so far
-  // Claiming a ticket (wave 0, one lane): the atomic's return lands in
-  // `ticket` asynchronously and is counted by vmcnt in issue order with the
-  // stage loads; it is read (written to s_ticket) only by the stage body
-  // NS - 2 stages later, after a vmcnt wait that leaves fewer loads
-  // outstanding than were issued after it.  Both steps are inline assembly so
-  // that nothing reads the register in between.
-  int ticket;  // written only by the claim, read only by the post that follows it
+  // Claiming a ticket (one lane of wave 0): an atomic fetch-add the compiler
+  // sees, so that it keeps the returned value's register reserved and waits
+  // for the return before the value is used.  It does not count the
+  // inline-assembly stage loads, so that wait is vmcnt(0); the compiler
+  // places it right after the claim (it moves the ticket to a scalar
+  // register), at the start of a read phase, where wave 0's loads in flight
+  // are the next stage's (needed by the end of the phase anyway) and the one
+  // after.  A few claims per workgroup and launch: measured +0.2-1% on the
+  // layer against an inline-assembly claim whose return was covered by the
+  // stage waits, which depended on the compiler never touching the ticket's
+  // register in between.  The post, NS - 1 stages later, copies the ticket
+  // to LDS for every wave.
+  int ticket = 0;  // written only by the claim, read only by the post that follows it
   int post_cnt = 0, post_slot = 0;
   auto claim = [&](int n) {
-    if (wave == 0) {
-      uint64_t save;
-      asm volatile(
-          "s_mov_b64 %1, exec\n\t"
-          "s_mov_b64 exec, 1\n\t"
-          "global_atomic_add %0, %2, %3, off sc0\n\t"
-          "s_mov_b64 exec, %1"
-          : "=&v"(ticket), "=&s"(save)
-          : "v"(sched), "v"(1)
-          : "memory");
-    }
+    if (wave == 0 && lane == 0) ticket = __hip_atomic_fetch_add(sched, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     post_cnt = NS - 1;
     post_slot = n & 3;
   };
   auto post = [&]() {
-    if (wave == 0) {
-      uint64_t save;
-      asm volatile(
-          "s_mov_b64 %0, exec\n\t"
-          "s_mov_b64 exec, 1\n\t"
-          "ds_write_b32 %1, %2\n\t"
-          "s_mov_b64 exec, %0"
-          : "=&s"(save)
-          : "v"(lds_address(&s_ticket[post_slot])), "v"(ticket)
-          : "memory");
-    }
+    if (wave == 0 && lane == 0) s_ticket[post_slot] = ticket;
   };
   __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferConfig);
   __amdgpu_buffer_rsrc_t b_rsrc = a_rsrc;
