@@ -183,3 +183,19 @@ def test_forward_noalloc_validation(lib):
     assert f(*big[:3], 1000, *big[4:]) == 2                          # d % 64
     assert f(*big[:4], 300, *big[5:]) == 2                           # E > 256
     assert f(*big[:9], 7, *big[10:]) == 1                            # bad dtype
+
+
+def test_device_checked_library_has_the_same_entry_points():
+    # libmoe_debug.so: the same kernels with the device-side contract checks
+    # compiled in; built beside libmoe.so
+    import os
+    if not os.path.exists(tre.DEBUG_LIB_PATH):
+        from token_routing_expert_amd import build as tre_build
+        tre_build.build(debug=True)
+    dbg = tre.open_library(tre.DEBUG_LIB_PATH)
+    for n in tre.exported_symbols():
+        assert hasattr(dbg, n), n
+    # host validation is shared: the same refusals, nothing launched
+    assert dbg.moe_route_topk(FAKE, 4, 8, 9, FAKE, FAKE, None) == 1
+    assert dbg.moe_forward_workspace_size(100, 128, 8, 2, 256, 1) == tre.load().moe_forward_workspace_size(
+        100, 128, 8, 2, 256, 1)

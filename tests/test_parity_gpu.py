@@ -8,6 +8,7 @@ routing and permutation in full and the layer output on sampled tokens, in
 the same launch configuration the benchmark times.
 """
 import gc
+import os
 
 import dataclasses
 
@@ -1079,3 +1080,57 @@ def test_training_step_saved_equals_recompute(tre, T, d, E, k, I, logits):
                           logits=inp.logits, pair_expert=inp.pair_expert, pair_w=inp.pair_w)
     for key, rkey in (("dx", "dx"), ("dw_gate_up", "dw_gate_up"), ("dw_down", "dw_down"), ("dtopk_w", "dw")):
         assert rel_l2(to_host(g_sv[key]), ref[rkey]) <= TOL["bf16"], key
+
+
+_DEBUG_LIB = []
+
+
+def debug_lib():
+    """libmoe_debug.so (the device-side contract checks compiled in), opened once."""
+    if not _DEBUG_LIB:
+        import token_routing_expert_amd as tre_mod
+        assert os.path.exists(tre_mod.DEBUG_LIB_PATH), "libmoe_debug.so is not built"
+        _DEBUG_LIB.append(tre_mod.open_library(tre_mod.DEBUG_LIB_PATH))
+    return _DEBUG_LIB[0]
+
+
+@pytest.mark.parametrize("T,d,E,k,I,dtype,logits", [
+    (8192, 1024, 64, 2, 512, "bf16", "normal"),      # tall tiles, claimed tail, split tail
+    (16000, 1024, 24, 1, 512, "bf16", "normal_bias"),  # one pair per token: the down projection writes the output
+    (3000, 256, 8, 1, 320, "bf16", None),            # given pairs with masked ones
+    (48, 256, 8, 2, 2048, "bf16", "normal"),         # few rows: 64-row tiles, k-split down projection
+    (257, 64, 3, 2, 64, "f32", "uniform"),
+])
+def test_device_checked_build_equals_release(tre, T, d, E, k, I, dtype, logits):
+    # Valid input only (a value outside its contract stops the checked build
+    # with a trap): the checked library computes the same layer, bit for bit.
+    torch = _torch()
+    dbg = debug_lib()
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype=dtype, seed=T + 7 * E, logits=logits,
+                                zero_experts=1 if logits is None else 0)
+    say(f"device-checked build T={T} d={d} E={E} k={k} I={I} {dtype} logits={logits}")
+    xd, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
+    dt = tre.MOE_F32 if dtype == "f32" else tre.MOE_BF16
+    if inp.logits is not None:
+        lg = to_device(inp.logits)
+        idx_a = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w_a = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    else:
+        lg = None
+        pe = inp.pair_expert.reshape(T, k).copy()
+        pe[::7] = -1   # masked pairs are within the contract
+        idx_a = to_device(pe)
+        w_a = to_device(inp.pair_w.reshape(T, k))
+    idx_b, w_b = idx_a.clone(), w_a.clone()
+    out_a, _, _ = tre.moe_forward(xd, wgu, wd, k, logits=lg, topk_idx=idx_a, topk_w=w_a)
+    out_b = torch.empty_like(out_a)
+    nbytes = dbg.moe_forward_workspace_size(T, d, E, k, I, dt)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    st = dbg.moe_forward(ptr(xd), ptr(lg), T, d, E, k, I, ptr(wgu), ptr(wd), dt, ptr(idx_b), ptr(w_b), None, None,
+                         None, ptr(out_b), ptr(ws), nbytes, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    sync()
+    view = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(idx_a, idx_b) and torch.equal(w_a, w_b)
+    assert torch.equal(out_a.view(view), out_b.view(view)), "the checked build's output differs"

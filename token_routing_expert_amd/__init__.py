@@ -22,6 +22,7 @@ import re
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
+DEBUG_LIB_PATH = os.path.join(PKG_DIR, "libmoe_debug.so")   # the same entry points, device checks compiled in
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "moe.h")
 
 MOE_F32 = 0
@@ -44,17 +45,11 @@ def exported_symbols() -> list[str]:
     return re.findall(r"^(?:moe_status|size_t|const char\*)\s+(moe_\w+)\s*\(", text, flags=re.M)
 
 
-def load(build_if_missing: bool = True):
-    """Load libmoe.so (building it first when it does not exist yet)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        if not build_if_missing:
-            raise RuntimeError(f"{LIB_PATH} is not built")
-        from . import build as _build
-        _build.build()
-    lib = ctypes.CDLL(LIB_PATH)
+def open_library(path: str):
+    """ctypes handle of a built library at `path` with every entry point's
+    signature declared (libmoe.so, or its device-checked twin
+    libmoe_debug.so, which has the same entry points)."""
+    lib = ctypes.CDLL(path)
     p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     st = ctypes.c_int
     sig = {
@@ -79,8 +74,21 @@ def load(build_if_missing: bool = True):
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = res
-    _lib = lib
     return lib
+
+
+def load(build_if_missing: bool = True):
+    """Load libmoe.so (building it first when it does not exist yet)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise RuntimeError(f"{LIB_PATH} is not built")
+        from . import build as _build
+        _build.build()
+    _lib = open_library(LIB_PATH)
+    return _lib
 
 
 # ---- marshalling helpers ----------------------------------------------------------

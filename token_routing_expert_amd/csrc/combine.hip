@@ -74,6 +74,7 @@ __device__ __forceinline__ void combine_token(const u32x4* __restrict__ y, int64
 #pragma unroll
   for (int j = 0; j < KS; ++j) {
     const int64_t r = j < k ? pair_row[t * k + j] : -1;
+    MOE_DCHECK(r >= -1 && r < max_rows);   // a grouped row, or -1 for a dropped pair
     live[j] = r >= 0 && r < max_rows;
     row[j] = live[j] ? r : 0;
     wt[j] = (j < k && pair_w) ? pair_w[t * k + j] : 1.f;
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const u32x4* __restrict__ 
     for (int i = 0; i < n; ++i) acc[i] = 0.f;
     for (int j = 0; j < k; ++j) {
       const int64_t r = pair_row[t * k + j];
+      MOE_DCHECK(r >= -1 && r < max_rows);
       if (r < 0 || r >= max_rows) continue;
       const float w = pair_w ? pair_w[t * k + j] : 1.f;
       float f[n];

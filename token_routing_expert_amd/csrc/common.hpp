@@ -37,6 +37,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Device-side contract checks.  The release library clamps every value it
+// reads on the device (expert ids, offsets, row indices) to the buffers it
+// indexes, so bad input gives bad output but never an out-of-range access.
+// Built with MOE_DEVICE_CHECKS (libmoe_debug.so), the kernels also stop at
+// the first value outside its contract, with a trap (no message: a printf
+// call inside the grouped GEMM's loop would cost it its scalar registers).
+// Only valid input may be given to that build.
+#ifdef MOE_DEVICE_CHECKS
+#define MOE_DCHECK(cond) \
+  do {                   \
+    if (!(cond)) __builtin_trap(); \
+  } while (0)
+#else
+#define MOE_DCHECK(cond) ((void)0)
+#endif
+
 template <typename T>
 __device__ __forceinline__ T clampi(T v, T lo, T hi) {
   return v < lo ? lo : (v > hi ? hi : v);

@@ -259,6 +259,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   int mt = 0;
   if (tid < E) {
     // offsets are int32, so the clamped values fit an int
+    MOE_DCHECK(0 <= offsets[tid] && offsets[tid] <= offsets[tid + 1] && offsets[tid + 1] <= max_rows);
     const int lo = (int)clampi<int64_t>(offsets[tid], 0, max_rows);
     const int hi = (int)clampi<int64_t>(offsets[tid + 1], lo, max_rows);
     s_lo[tid] = lo;
@@ -271,6 +272,14 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   const int start = block_exclusive_scan<WAVES>(mt, s_wave, &total_mt);
   if (tid < E) s_start[tid] = start;
   __syncthreads();
+#ifdef MOE_DEVICE_CHECKS
+  // (device-checked build) every grouped row's token, spread over the grid
+  if (row_token) {
+    const int64_t n_rows = clampi<int64_t>(offsets[E], 0, max_rows);
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + tid; r < n_rows; r += (int64_t)gridDim.x * blockDim.x)
+      MOE_DCHECK(row_token[r] >= 0 && row_token[r] < a_rows);
+  }
+#endif
   const int64_t total_tiles = (int64_t)total_mt * n_tiles;
   const int G = gridDim.x;
   const int vb = (blockIdx.x % kXcd) * (G / kXcd) + blockIdx.x / kXcd;

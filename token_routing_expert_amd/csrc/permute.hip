@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kThreads) void k_perm_hist(const int32_t* __restric
     const int64_t p = base + i;
     if (p < P) {
       const int e = pair_expert[p];
+      MOE_DCHECK(e >= -1 && e < E);   // an expert id, or -1 for a masked pair
       if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
   }
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_perm_small(const int32_t* __r
   for (int j = 0; j < kSmallSteps; ++j) {
     const int p = j * kSmallThreads + tid;
     ids[j] = p < P ? pair_expert[p] : -1;
+    MOE_DCHECK(ids[j] >= -1 && ids[j] < E);   // an expert id, or -1 for a masked pair
   }
   if (tid < E) cnt[tid] = 0;
   lds_barrier();

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   for (int s = 0; s < S; ++s) {
     const int e = s * G + lane;
     lg[s] = (active && e < E) ? logits[t * E + e] : 0.f;
+    MOE_DCHECK(__builtin_isfinite(lg[s]));   // logits are finite
   }
   route_token<G, S>(lg, t, active, E, k, topk_idx, topk_w);
 }
