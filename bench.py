@@ -385,9 +385,11 @@ def main() -> int:
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="MiB of scratch read before every timed step (0: no flush)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the router projection, permute-with-rows, graph and backward measurements")
-    ap.add_argument("--extras", default="graph,permute,router,backward",
-                    help="comma-separated measurements beside the layer (graph, permute, router, backward); "
+                    help="skip the router projection, permute-with-rows, graph, backward and tiled-weight "
+                         "measurements")
+    ap.add_argument("--extras", default="graph,permute,router,backward,tiled",
+                    help="comma-separated measurements beside the layer (graph, permute, router, backward, "
+                         "tiled); "
                          "--no-extras is the same as none")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
@@ -438,7 +440,7 @@ def main() -> int:
     kernels, work, peak_mm = kernel_table(inp, t["stage_ms"], n_rows, live)
     roofline = roofline_of(inp, kernels, work, peak_mm, args.workload)
 
-    graph_ms = permute_rows = router = backward = None
+    graph_ms = permute_rows = router = backward = tiled = None
     extras = set() if args.no_extras else {e for e in args.extras.split(",") if e and e != "none"}
     if extras:
         if "graph" in extras:
@@ -577,6 +579,35 @@ def main() -> int:
                                           "pairs_per_s": P / (step_ms * 1e-3)}}
             del gdx, gwgu, gwd, bws, gout
 
+        # ---- timed region 7 (beside the layer): the same layer on the expert
+        # weights in the column-tiled layout (moe_tile_weights, done once, then
+        # moe_forward_tiled; bit-identical output) ----
+        if "tiled" in extras and inp.dtype == "bf16":
+            wgu_t, wd_t = torch.empty_like(wgu), torch.empty_like(wd)
+            t_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            torch.cuda.synchronize()
+            t_ev[0].record(stream)
+            if lib.moe_tile_weights(ptr(wgu), ptr(wd), E, d, I, dt, ptr(wgu_t), ptr(wd_t), sp) != 0:
+                raise RuntimeError("moe_tile_weights failed")
+            t_ev[1].record(stream)
+            torch.cuda.synchronize()
+            tile_ms = t_ev[0].elapsed_time(t_ev[1])
+
+            def run_tiled():
+                st = lib.moe_forward_tiled(ptr(x), ptr(logits), T, d, E, k, I, ptr(wgu_t), ptr(wd_t), dt,
+                                           ptr(layer.topk_idx), ptr(layer.topk_w), None, None, None, ptr(layer.out),
+                                           ptr(layer.fws), layer.fws_bytes, sp)
+                if st != 0:
+                    raise RuntimeError(f"moe_forward_tiled failed with status {st}")
+            for _ in range(args.warmup):
+                run_tiled()
+            tl_ms = timed_cold(run_tiled, args.steps)
+            tiled = {"ms_per_step": round(tl_ms, 5), "pairs_per_s": P / (tl_ms * 1e-3),
+                     "tile_weights_ms": round(tile_ms, 4),
+                     "note": "moe_forward_tiled on weights laid out once by moe_tile_weights (a read and a write "
+                             "of every weight, outside the steps); output bit-identical to moe_forward"}
+            del wgu_t, wd_t
+
     result = {
         "metric": METRIC,
         "value": P / (ms_per_step * 1e-3),
@@ -608,6 +639,7 @@ def main() -> int:
         "permute_rows": permute_rows,
         "router_projection": router,
         "backward": backward,
+        "tiled_weights": tiled,
     }
     extras = [] if args.extra in ("", "none") else [w for w in args.extra.split(",") if w != args.workload]
     if extras:

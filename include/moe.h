@@ -180,6 +180,32 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
                        int32_t* pair_row, void* out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ---- column-tiled expert weights (inference) ---------------------------------
+ * The expert weights in the layout the grouped products stream them in: each
+ * expert's weight is stored as one block per 256-column tile of its product,
+ * so that a tile's k-stage is one contiguous run of memory (the pages' layout
+ * puts it in K separate pieces of a row).  A permutation of the elements: the
+ * tiled arrays have the sizes of the originals.  For expert e:
+ *   gate/up, tile c = 0 .. ceil(I/128)-1, n0 = 128 c, w = min(128, I - n0):
+ *     block [d][2w] at element e*d*2I + d*2*n0, row r =
+ *     Wgu[e][r][n0 .. n0+w) followed by Wgu[e][r][I+n0 .. I+n0+w);
+ *   down, tile c = 0 .. ceil(d/256)-1, n0 = 256 c, w = min(256, d - n0):
+ *     block [I][w] at element e*I*d + I*n0, row r = Wd[e][r][n0 .. n0+w).
+ * moe_tile_weights writes them (once, e.g. when a model is loaded: a read and
+ * a write of every weight); moe_forward_tiled is moe_forward on them, with
+ * results bit-identical to moe_forward on the original weights.  bf16 only.
+ *   w_gate_up [E, d, 2I], w_down [E, I, d] bf16 (inputs, unchanged)
+ *   w_gate_up_tiled, w_down_tiled: outputs of the same sizes
+ * Errors: as moe_forward's shape checks; MOE_ERR_UNSUPPORTED for MOE_F32;
+ * MOE_ERR_ARG for NULL pointers.  The forward's arguments and workspace are
+ * moe_forward's.                                                            */
+moe_status moe_tile_weights(const void* w_gate_up, const void* w_down, int32_t E, int32_t d, int32_t I, moe_dtype dt,
+                            void* w_gate_up_tiled, void* w_down_tiled, void* stream);
+moe_status moe_forward_tiled(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                             int32_t I, const void* w_gate_up_tiled, const void* w_down_tiled, moe_dtype dt,
+                             int32_t* topk_idx, float* topk_w, int32_t* expert_offsets, int32_t* row_token,
+                             int32_t* pair_row, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The layer as moe_forward computes it (same kernels, same results bit for
  * bit), for callers that cannot allocate memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  There is

@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol(lib):
         "moe_status_string", "moe_route_topk", "moe_permute_workspace_size", "moe_permute",
         "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
         "moe_forward_workspace_size", "moe_forward", "moe_gate_up_swiglu", "moe_down_proj", "moe_route_project",
-        "moe_backward_workspace_size", "moe_backward", "moe_forward_train", "moe_forward_noalloc"}
+        "moe_backward_workspace_size", "moe_backward", "moe_forward_train", "moe_forward_noalloc",
+        "moe_tile_weights", "moe_forward_tiled"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -199,3 +200,19 @@ def test_device_checked_library_has_the_same_entry_points():
     assert dbg.moe_route_topk(FAKE, 4, 8, 9, FAKE, FAKE, None) == 1
     assert dbg.moe_forward_workspace_size(100, 128, 8, 2, 256, 1) == tre.load().moe_forward_workspace_size(
         100, 128, 8, 2, 256, 1)
+
+
+def test_tile_weights_validation(lib):
+    f = lib.moe_tile_weights
+    assert f(FAKE, FAKE, 8, 128, 256, 0, FAKE, FAKE, None) == 2     # float32: bf16 only
+    assert f(FAKE, FAKE, 8, 96, 256, 1, FAKE, FAKE, None) == 2      # d % 64
+    assert f(FAKE, FAKE, 300, 128, 256, 1, FAKE, FAKE, None) == 2   # E > 256
+    assert f(FAKE, FAKE, 0, 128, 256, 1, FAKE, FAKE, None) == 1     # E < 1
+    assert f(FAKE, FAKE, 8, 128, 256, 5, FAKE, FAKE, None) == 1     # bad dtype
+    assert f(FAKE, None, 8, 128, 256, 1, FAKE, FAKE, None) == 1     # NULL weight
+    assert f(FAKE, FAKE, 8, 128, 256, 1, FAKE, None, None) == 1     # NULL output
+    g = lib.moe_forward_tiled
+    assert g(FAKE, None, 4, 128, 8, 2, 256, FAKE, FAKE, 0, FAKE, FAKE, None, None, None, FAKE, FAKE, 1 << 20,
+             None) == 2                                               # float32: bf16 only
+    assert g(FAKE, None, 0, 128, 8, 2, 256, FAKE, FAKE, 1, FAKE, FAKE, None, None, None, FAKE, None, 0,
+             None) == 0                                               # T == 0: nothing to do

@@ -1134,3 +1134,79 @@ def test_device_checked_build_equals_release(tre, T, d, E, k, I, dtype, logits):
     view = torch.int32 if dtype == "f32" else torch.int16
     assert torch.equal(idx_a, idx_b) and torch.equal(w_a, w_b)
     assert torch.equal(out_a.view(view), out_b.view(view)), "the checked build's output differs"
+
+
+def tiled_reference(w, gate_up: bool) -> np.ndarray:
+    """The column-tiled layout of include/moe.h, built on the host from its
+    definition: per expert, one [K][width] block per column tile (gate/up:
+    128 gate columns then the same up columns; down: 256 columns)."""
+    E, K, cols = w.shape
+    N = cols // 2 if gate_up else cols
+    tc = 128 if gate_up else 256
+    out = np.empty((E, K * cols), dtype=w.dtype)
+    for e in range(E):
+        parts = []
+        for n0 in range(0, N, tc):
+            wc = min(tc, N - n0)
+            blk = np.concatenate([w[e][:, n0:n0 + wc], w[e][:, N + n0:N + n0 + wc]], axis=1) if gate_up \
+                else w[e][:, n0:n0 + wc]
+            parts.append(blk.reshape(-1))
+        out[e] = np.concatenate(parts)
+    return out.reshape(w.shape)
+
+
+@pytest.mark.parametrize("E,d,I", [(3, 320, 320), (2, 128, 1024), (4, 2880, 192)])
+def test_tile_weights_layout(tre, E, d, I):
+    torch = _torch()
+    inp = workloads.make_custom(T=4, d=d, E=E, k=1, I=I, dtype="bf16", seed=E + d + I)
+    wgu, wd = to_device(inp.w_gate_up), to_device(inp.w_down)
+    wgu_t, wd_t = tre.moe_tile_weights(wgu, wd)
+    sync()
+    got_gu = wgu_t.view(torch.int16).cpu().numpy().view(np.uint16)
+    got_dn = wd_t.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got_gu, tiled_reference(inp.w_gate_up, True))
+    assert np.array_equal(got_dn, tiled_reference(inp.w_down, False))
+
+
+@pytest.mark.parametrize("T,d,E,k,I,logits", [
+    (8192, 1024, 64, 2, 512, "normal"),        # tall tiles, claimed and split tails
+    (16000, 1024, 24, 1, 512, "normal_bias"),  # one pair per token: the down projection writes the output
+    (1000, 192, 7, 3, 320, "normal"),          # 128-row tiles, partial column tiles
+    (48, 256, 8, 2, 2048, "normal"),           # 64-row tiles, k-split down projection
+    (3000, 256, 8, 1, 320, None),              # given pairs
+])
+def test_forward_tiled_equals_forward(tre, T, d, E, k, I, logits):
+    # the layer on column-tiled weights reads the same values into the same
+    # places: bit for bit the layer on the original weights
+    torch = _torch()
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + 3 * E, logits=logits)
+    say(f"tiled weights T={T} d={d} E={E} k={k} I={I} logits={logits}")
+    xd, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
+    wgu_t, wd_t = tre.moe_tile_weights(wgu, wd)
+    kw = {}
+    if inp.logits is not None:
+        kw["logits"] = to_device(inp.logits)
+    else:
+        kw["topk_idx"] = to_device(inp.pair_expert.reshape(T, k))
+        kw["topk_w"] = to_device(inp.pair_w.reshape(T, k))
+    out_a, idx_a, w_a = tre.moe_forward(xd, wgu, wd, k, **kw)
+    out_b, idx_b, w_b = tre.moe_forward_tiled(xd, wgu_t, wd_t, k, **kw)
+    sync()
+    assert torch.equal(idx_a, idx_b) and torch.equal(w_a, w_b)
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16)), "tiled weights change the layer"
+
+
+@pytest.mark.parametrize("name", ["large_e128", "decode"])
+def test_forward_tiled_full_size(tre, name):
+    torch = _torch()
+    inp = workload(name)
+    say(f"tiled weights, full {name}")
+    xd, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
+    wgu_t, wd_t = tre.moe_tile_weights(wgu, wd)
+    lg = to_device(inp.logits)
+    out_a, _, _ = tre.moe_forward(xd, wgu, wd, inp.k, logits=lg)
+    out_b, _, _ = tre.moe_forward_tiled(xd, wgu_t, wd_t, inp.k, logits=lg)
+    sync()
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    del xd, wgu, wd, wgu_t, wd_t, out_a, out_b
+    torch.cuda.empty_cache()

@@ -13,6 +13,7 @@ Functions carry the C entry points' names:
   moe_gate_up_swiglu / moe_down_proj   its two halves
   moe_combine       routing-weighted sum back to token order
   moe_forward       the whole layer
+  moe_tile_weights / moe_forward_tiled   the layer on column-tiled weights
 """
 from __future__ import annotations
 
@@ -69,6 +70,8 @@ def open_library(path: str):
         "moe_backward": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, p, i32, p, sz, p], st),
         "moe_forward_train": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, sz, p], st),
         "moe_forward_noalloc": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p], st),
+        "moe_tile_weights": ([p, p, i32, i32, i32, st, p, p, p], st),
+        "moe_forward_tiled": ([p, p, i32, i32, i32, i32, i32, p, p, st, p, p, p, p, p, p, p, sz, p], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -306,7 +309,7 @@ def moe_forward_workspace_size(T: int, d: int, E: int, k: int, I: int, dtype) ->
 
 
 def moe_forward(x, w_gate_up, w_down, k: int, logits=None, topk_idx=None, topk_w=None, out=None,
-                expert_offsets=None, row_token=None, pair_row=None, workspace=None, stream=None):
+                expert_offsets=None, row_token=None, pair_row=None, workspace=None, stream=None, _tiled=False):
     """The whole layer.  With ``logits`` [T, E] the layer routes first (topk_idx / topk_w are
     outputs); without, ``topk_idx`` / ``topk_w`` [T, k] are the given pairs.
     Returns (out [T, d], topk_idx, topk_w)."""
@@ -336,10 +339,32 @@ def moe_forward(x, w_gate_up, w_down, k: int, logits=None, topk_idx=None, topk_w
     dt = _dt(x)
     nbytes = lib.moe_forward_workspace_size(T, d, E, k, I, dt)
     ws = _workspace(nbytes, x, workspace)
-    _check("moe_forward", lib.moe_forward(_ptr(x), _ptr(logits), T, d, E, k, I, _ptr(w_gate_up), _ptr(w_down), dt,
-                                          _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token),
-                                          _ptr(pair_row), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    fn, name = (lib.moe_forward_tiled, "moe_forward_tiled") if _tiled else (lib.moe_forward, "moe_forward")
+    _check(name, fn(_ptr(x), _ptr(logits), T, d, E, k, I, _ptr(w_gate_up), _ptr(w_down), dt, _ptr(topk_idx),
+                    _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token), _ptr(pair_row), _ptr(out), _ptr(ws), nbytes,
+                    _stream(stream)))
     return out, topk_idx, topk_w
+
+
+def moe_tile_weights(w_gate_up, w_down, stream=None):
+    """The expert weights in the column-tiled layout (include/moe.h): new
+    tensors of the same shapes, for moe_forward_tiled.  bf16 only."""
+    torch = _torch()
+    lib = load()
+    E, d, two_i = w_gate_up.shape
+    I = two_i // 2
+    if two_i != 2 * I:
+        raise ValueError(f"w_gate_up {tuple(w_gate_up.shape)}: the last dimension is 2I")
+    _expect(w_down, w_gate_up.dtype, (E, I, d), "w_down")
+    wgu_t, wd_t = torch.empty_like(w_gate_up), torch.empty_like(w_down)
+    _check("moe_tile_weights", lib.moe_tile_weights(_ptr(w_gate_up), _ptr(w_down), E, d, I, _dt(w_gate_up),
+                                                    _ptr(wgu_t), _ptr(wd_t), _stream(stream)))
+    return wgu_t, wd_t
+
+
+def moe_forward_tiled(x, w_gate_up_tiled, w_down_tiled, k: int, **kw):
+    """moe_forward on weights from moe_tile_weights (same arguments and results)."""
+    return moe_forward(x, w_gate_up_tiled, w_down_tiled, k, _tiled=True, **kw)
 
 
 def noalloc_scratch_bytes() -> int:

@@ -282,10 +282,11 @@ moe_status check_forward_args(const void* x, const float* logits, int32_t T, int
 }
 
 // The layer (moe_forward's work) with its scratch in `workspace`.
+// wtiled: the expert weights are in the column-tiled layout of moe_tile_weights.
 moe_status forward_impl(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
                         const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
                         int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row, void* out, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, bool wtiled = false) {
   TRY(check_forward_args(x, logits, T, d, E, k, I, w_gate_up, w_down, dt, topk_idx, topk_w, out));
   if (T == 0) return MOE_OK;
   const int64_t P = (int64_t)T * k;
@@ -315,14 +316,14 @@ moe_status forward_impl(const void* x, const float* logits, int32_t T, int32_t d
     // the gate/up projection reads the token rows in place through row_token
     // (no expert-ordered copy of x is materialised)
     TRY(from_hip(launch_gate_up_bf16((const bf16_t*)x, offs, P, E, d, I, (const bf16_t*)w_gate_up, (bf16_t*)h, s,
-                                     r_tok, T, sched)));
+                                     r_tok, T, sched, wtiled)));
     if (scatter) {
       const DownScatter sc{(bf16_t*)out, r_tok, row_w, T};
       return from_hip(launch_down_bf16((const bf16_t*)h, offs, P, E, d, I, (const bf16_t*)w_down, nullptr, s,
-                                       (float*)(ws + L.split), sched, &sc));
+                                       (float*)(ws + L.split), sched, &sc, false, wtiled));
     }
     TRY(from_hip(launch_down_bf16((const bf16_t*)h, offs, P, E, d, I, (const bf16_t*)w_down, (bf16_t*)y_perm, s,
-                                  (float*)(ws + L.split), sched)));
+                                  (float*)(ws + L.split), sched, nullptr, false, wtiled)));
     return from_hip(launch_combine_bf16((const bf16_t*)y_perm, P, p_row, topk_w, T, k, d, (bf16_t*)out, s));
   }
   TRY(from_hip(launch_permute_rows(topk_idx, T, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, nullptr, x,
@@ -374,6 +375,28 @@ moe_status moe_forward(const void* x, const float* logits, int32_t T, int32_t d,
                        size_t workspace_bytes, void* stream) {
   return forward_impl(x, logits, T, d, E, k, I, w_gate_up, w_down, dt, topk_idx, topk_w, expert_offsets, row_token,
                       pair_row, out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_tile_weights(const void* w_gate_up, const void* w_down, int32_t E, int32_t d, int32_t I, moe_dtype dt,
+                            void* w_gate_up_tiled, void* w_down_tiled, void* stream) {
+  if (!dtype_ok(dt)) return MOE_ERR_ARG;
+  TRY(check_experts(E));
+  TRY(check_width(d));
+  TRY(check_width(I));
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d * I * 2 * 2 >= kMaxElems) return MOE_ERR_UNSUPPORTED;   // one expert's gate/up bytes
+  if (!w_gate_up || !w_down || !w_gate_up_tiled || !w_down_tiled) return MOE_ERR_ARG;
+  return from_hip(launch_tile_weights_bf16((const bf16_t*)w_gate_up, (const bf16_t*)w_down, E, d, I,
+                                           (bf16_t*)w_gate_up_tiled, (bf16_t*)w_down_tiled, (hipStream_t)stream));
+}
+
+moe_status moe_forward_tiled(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
+                             int32_t I, const void* w_gate_up_tiled, const void* w_down_tiled, moe_dtype dt,
+                             int32_t* topk_idx, float* topk_w, int32_t* expert_offsets, int32_t* row_token,
+                             int32_t* pair_row, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dt == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  return forward_impl(x, logits, T, d, E, k, I, w_gate_up_tiled, w_down_tiled, dt, topk_idx, topk_w, expert_offsets,
+                      row_token, pair_row, out, workspace, workspace_bytes, stream, true);
 }
 
 moe_status moe_forward_noalloc(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,

@@ -206,9 +206,11 @@ hipError_t launch_sched_reset(int32_t* sched, hipStream_t s);
 // h: [max_rows, I] of the activation type.
 // With row_token, activation row r is row row_token[r] of x ([x_rows, d]):
 // the permutation's row move happens inside the load.  Without, x is x_perm.
+// wtiled: the weights are in the column-tiled layout of launch_tile_weights_bf16.
 hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s,
-                               const int32_t* row_token = nullptr, int64_t x_rows = 0, int32_t* sched = nullptr);
+                               const int32_t* row_token = nullptr, int64_t x_rows = 0, int32_t* sched = nullptr,
+                               bool wtiled = false);
 // split_ws (optional, split_workspace(max_rows, E, d, I) bytes, float32):
 // with few rows the down projection's k-stages are split over more
 // workgroups and summed there in a fixed order (deterministic); with many,
@@ -231,7 +233,8 @@ bool down_scatters(int64_t max_rows, int E, int d, int I, bool have_split_ws);
 // equal, bit for bit, what the scatter path computes.
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws = nullptr,
-                            int32_t* sched = nullptr, const DownScatter* sc = nullptr, bool scatter_tiles = false);
+                            int32_t* sched = nullptr, const DownScatter* sc = nullptr, bool scatter_tiles = false,
+                            bool wtiled = false);
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
                               int d, int I, const float* w_gate_up, float* h, hipStream_t s);
 hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
@@ -239,7 +242,13 @@ hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_
 hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets,
                                    int64_t max_rows, int E, int d, int I, const bf16_t* w_gate_up,
                                    const bf16_t* w_down, bf16_t* h, bf16_t* y_perm, hipStream_t s,
-                                   float* split_ws = nullptr, int32_t* sched = nullptr);
+                                   float* split_ws = nullptr, int32_t* sched = nullptr, bool wtiled = false);
+// Both expert weights in the column-tiled layout the forward products can
+// read instead (same sizes; a permutation of the elements): each expert's
+// weight stored as one [K][width] block per 256-column tile of the product,
+// for gate/up 128 gate columns followed by the same 128 up columns.
+hipError_t launch_tile_weights_bf16(const bf16_t* w_gate_up, const bf16_t* w_down, int E, int d, int I,
+                                    bf16_t* wgu_tiled, bf16_t* wd_tiled, hipStream_t s);
 hipError_t launch_grouped_ffn_f32(const float* x_perm, const int32_t* expert_offsets,
                                   int64_t max_rows, int E, int d, int I, const float* w_gate_up,
                                   const float* w_down, float* h, float* y_perm, hipStream_t s);

@@ -46,12 +46,16 @@
 // workloads).
 #include "common.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace tre {
 namespace {
 
 constexpr int kXcd = 8;          // XCDs per MI355X; workgroups are dealt round-robin over them
+// column-tiled weights: the columns a gate/up tile takes from each half, and
+// a down tile's columns (the forward products' 256-column tiles)
+constexpr int kTileGateCols = 128, kTileDownCols = 256;
 // byte offset that is always past num_records (a buffer load there returns zeros)
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int64_t max_rows, int E, int K, int N, int ldw,
     const bf16_t* __restrict__ W, bf16_t* __restrict__ Out, int n_tiles, const int32_t* __restrict__ row_token,
     int64_t a_rows, bf16_t* __restrict__ Out2, const bf16_t* __restrict__ Aux, int n_split_arg,
-    float* __restrict__ Part, int32_t* __restrict__ sched, const float* __restrict__ row_w) {
+    float* __restrict__ Part, int32_t* __restrict__ sched, const float* __restrict__ row_w, int wtiled) {
   // (k-split ranges are only used with the lockstep tiles: the ping-pong
   // instances see one range per tile, a constant)
   const int n_split = PP ? 1 : n_split_arg;
@@ -195,6 +199,8 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   constexpr int BNO = SWIGLU ? BNB / 2 : BNB;  // output columns per tile
   constexpr int WCOL = 32 * NJ;                 // weight columns per wave
   static_assert(NS >= 3 && NS <= 5, "a ring of 3 to 5 stages");
+  static_assert(BT || (SWIGLU ? BNB == 2 * kTileGateCols : BNB == kTileDownCols),
+                "column-tiled weights are blocked for the products' tile width");
   static_assert(BM <= 256, "one index DMA covers 256 rows");
   static_assert(!PP || WAVES == 8, "ping-pong pairs two groups of four waves, one wave of each per SIMD");
   // With kEpiScatter the tile's row -> token map (and row weights) serve
@@ -436,7 +442,8 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   // buffers: scalar, added to every lane's offset by the load itself
   uint32_t ka = 0, kb = 0;
   constexpr uint32_t kAStep = BK * 2;
-  const uint32_t kb_step = BT ? (uint32_t)BK * 2u : (uint32_t)BK * (uint32_t)ldw * 2u;
+  // (per tile with column-tiled weights: the tile's block is [K][width])
+  uint32_t kb_step = BT ? (uint32_t)BK * 2u : (uint32_t)BK * (uint32_t)ldw * 2u;
   const uint32_t a_lds0 = lds_address(sA) + wave * 1024;
   const uint32_t b_lds0 = lds_address(sB) + wave * 1024;
 
@@ -483,10 +490,20 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
         uniform_ptr(gather ? (const void*)A : (const void*)(A + t.row0 * K)), (short)0,
         __builtin_amdgcn_readfirstlane(gather ? (int)(a_rows * K * 2) : t.rows * K * 2), kBufferConfig);
     // one expert's weights: [K][ldw] (read transposed by the LDS reads), or
-    // with BT [N][K] (rows of k, read like the activations)
+    // with BT [N][K] (rows of k, read like the activations).  Column-tiled
+    // weights (wtiled, [K][N] products only): the expert's ldw columns are
+    // stored as one block per column tile, block c holding the tile's
+    // columns as [K][width] -- for gate/up its gate columns, then the
+    // matching up columns -- so a k-stage of a tile is one contiguous run.
+    // The descriptor then spans the tile's block only.
     const int64_t w_elems = BT ? (int64_t)N * K : (int64_t)K * ldw;
-    b_rsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(W + (int64_t)t.e * w_elems), (short)0,
-                                               __builtin_amdgcn_readfirstlane((int)(w_elems * 2)), kBufferConfig);
+    const int t_width = SWIGLU ? 2 * min(BNB / 2, N - t.n0) : min(BNB, N - t.n0);  // the tile's weight columns
+    const bool tiled = !BT && wtiled;
+    const int64_t w_base = (int64_t)t.e * w_elems + (tiled ? (int64_t)K * (SWIGLU ? 2 * t.n0 : t.n0) : 0);
+    b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(W + w_base), (short)0,
+        __builtin_amdgcn_readfirstlane(tiled ? K * t_width * 2 : (int)(w_elems * 2)), kBufferConfig);
+    if (tiled) kb_step = __builtin_amdgcn_readfirstlane((uint32_t)BK * (uint32_t)t_width * 2u);
     // (double-stages: instruction p of this wave fills rows (wave + WAVES p)
     // 8 + lane / 8 with 64 k-values each, chunk lane % 8 of the LDS row)
     constexpr int ARPI = AD ? GD::RPI : GE::RPI, ACPR = AD ? GD::CPR : GE::CPR;
@@ -529,14 +546,14 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
       int gcol;
       bool ok;
       if (SWIGLU) {
-        const int hc = t.n0 + (tc % (BNB / 2));
-        ok = hc < N;
-        gcol = (tc < BNB / 2) ? hc : N + hc;
+        const int hc = tc % (BNB / 2);   // the gate or up column within the tile
+        ok = t.n0 + hc < N;
+        gcol = tiled ? ((tc < BNB / 2) ? hc : t_width / 2 + hc) : ((tc < BNB / 2) ? t.n0 + hc : N + t.n0 + hc);
       } else {
-        gcol = t.n0 + tc;
-        ok = gcol < N;
+        gcol = tiled ? tc : t.n0 + tc;
+        ok = t.n0 + tc < N;
       }
-      b_voff[p] = ok ? (uint32_t)(kr * ldw + gcol) * 2u : kOutOfRange;
+      b_voff[p] = ok ? (uint32_t)(kr * (tiled ? t_width : ldw) + gcol) * 2u : kOutOfRange;
     }
     int k0, k1;
     unit_range(inext_u, k0, k1);
@@ -1294,14 +1311,16 @@ template <int EPI, bool BT = false, int BK = 32, int OCC = 2, int NJ = 4, int WM
 hipError_t launch_dma(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                       const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
                       int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr, int n_split = 1,
-                      float* part = nullptr, int32_t* sched = nullptr, const float* row_w = nullptr) {
+                      float* part = nullptr, int32_t* sched = nullptr, const float* row_w = nullptr,
+                      bool wtiled = false) {
   constexpr bool SWIGLU = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
   constexpr int BNO = SWIGLU ? 32 * NJ : 64 * NJ;   // output columns per tile
   if (K / BK / n_split < NS - 1) return hipErrorInvalidValue;  // each range spans at least NS - 1 stages
   const int nt = (int)ceil_div(N, BNO);
   dma::k_grouped_gemm<EPI, BT, BK, OCC, NJ, WM, NS, PP, TL>
       <<<persistent_grid(max_rows, E, 64 * WM, nt * n_split, OCC), 128 * WM, 0, s>>>(
-          a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows, out2, aux, n_split, part, sched, row_w);
+          a, offsets, max_rows, E, K, N, ldw, w, out, nt, row_token, a_rows, out2, aux, n_split, part, sched, row_w,
+          wtiled ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1414,7 +1433,8 @@ template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token = nullptr,
                        int64_t a_rows = 0, bf16_t* out2 = nullptr, const bf16_t* aux = nullptr,
-                       int32_t* sched = nullptr, float* tail_ws = nullptr, bool allow_tall = true);
+                       int32_t* sched = nullptr, float* tail_ws = nullptr, bool allow_tall = true,
+                       bool wtiled = false);
 
 // 256-row tiles (8 waves in ping-pong, one workgroup per CU: each weight
 // stage feeds twice the rows) once the experts hold 128 rows or more on
@@ -1439,25 +1459,27 @@ bool tall_tiles(int64_t max_rows, int E) { return max_rows <= 384 * (int64_t)E; 
 template <int EPI, bool BT>
 hipError_t launch_auto(const bf16_t* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N, int ldw,
                        const bf16_t* w, bf16_t* out, hipStream_t s, const int32_t* row_token, int64_t a_rows,
-                       bf16_t* out2, const bf16_t* aux, int32_t* sched, float* tail_ws, bool allow_tall) {
+                       bf16_t* out2, const bf16_t* aux, int32_t* sched, float* tail_ws, bool allow_tall,
+                       bool wtiled) {
   if constexpr (EPI == kEpiPlain && !BT) {
     if (allow_tall && big_tiles(max_rows, E, K) && tall_tiles(max_rows, E) && row_token == nullptr)
       return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, nullptr,
-                                                             0, out2, aux, 1, tail_ws, sched);
+                                                             0, out2, aux, 1, tail_ws, sched, nullptr, wtiled);
   }
   if constexpr (EPI == kEpiSwiglu && !BT) {
     if (big_tiles(max_rows, E, K) && tall_tiles(max_rows, E))
       return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
-                                                             a_rows, out2, aux, 1, nullptr, sched);
+                                                             a_rows, out2, aux, 1, nullptr, sched, nullptr, wtiled);
   }
   if (big_tiles(max_rows, E, K))
     return launch_dma<EPI, BT, 32, 1, 4, 4, 4, true>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
                                                      a_rows, out2, aux, 1, EPI == kEpiPlain && !BT ? tail_ws : nullptr,
-                                                     sched);
+                                                     sched, nullptr, wtiled);
   if (small_tiles(max_rows, E))
     return launch_dma<EPI, BT, 32, 2, 4, 1, 3, false>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token,
-                                                      a_rows, out2, aux);
-  return launch_dma<EPI, BT>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token, a_rows, out2, aux);
+                                                      a_rows, out2, aux, 1, nullptr, nullptr, nullptr, wtiled);
+  return launch_dma<EPI, BT>(a, offsets, max_rows, E, K, N, ldw, w, out, s, row_token, a_rows, out2, aux, 1, nullptr,
+                             nullptr, nullptr, wtiled);
 }
 
 }  // namespace
@@ -1473,9 +1495,9 @@ hipError_t launch_sched_reset(int32_t* sched, hipStream_t s) {
 
 hipError_t launch_gate_up_bf16(const bf16_t* x, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                                int I, const bf16_t* w_gate_up, bf16_t* h, hipStream_t s, const int32_t* row_token,
-                               int64_t x_rows, int32_t* sched) {
+                               int64_t x_rows, int32_t* sched, bool wtiled) {
   return launch_auto<kEpiSwiglu, false>(x, expert_offsets, max_rows, E, d, I, 2 * I, w_gate_up, h, s, row_token,
-                                        x_rows, nullptr, nullptr, sched);
+                                        x_rows, nullptr, nullptr, sched, nullptr, true, wtiled);
 }
 
 // Whether the 256-row down projection can have a split tail: only when its
@@ -1502,7 +1524,7 @@ bool down_scatters(int64_t max_rows, int E, int d, int I, bool have_split_ws) {
 
 hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                             int I, const bf16_t* w_down, bf16_t* y_perm, hipStream_t s, float* split_ws,
-                            int32_t* sched, const DownScatter* sc, bool scatter_tiles) {
+                            int32_t* sched, const DownScatter* sc, bool scatter_tiles, bool wtiled) {
   if (sc && !down_scatters(max_rows, E, d, I, split_ws != nullptr)) return hipErrorInvalidValue;
   {
     const bool small = small_tiles(max_rows, E);
@@ -1511,9 +1533,10 @@ hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int6
       const hipError_t e =
           small ? launch_dma<kEpiPartial, false, 32, 2, 4, 1, 3, false>(h, expert_offsets, max_rows, E, I, d, d,
                                                                         w_down, nullptr, s, nullptr, 0, nullptr,
-                                                                        nullptr, n_split, split_ws)
+                                                                        nullptr, n_split, split_ws, nullptr, nullptr,
+                                                                        wtiled)
                 : launch_dma<kEpiPartial>(h, expert_offsets, max_rows, E, I, d, d, w_down, nullptr, s, nullptr, 0,
-                                          nullptr, nullptr, n_split, split_ws);
+                                          nullptr, nullptr, n_split, split_ws, nullptr, nullptr, wtiled);
       if (e != hipSuccess) return e;
       const dim3 grid((unsigned)ceil_div(d / 4, 256), (unsigned)max_rows);
       k_split_sum<<<grid, 256, 0, s>>>(split_ws, n_split, expert_offsets, E, max_rows, d, sc ? sc->out : y_perm,
@@ -1528,10 +1551,10 @@ hipError_t launch_down_bf16(const bf16_t* h, const int32_t* expert_offsets, int6
   if (sc)   // 256-row tiles (down_scatters)
     e = launch_dma<kEpiScatter, false, 32, 1, 4, 4, 4, true>(h, expert_offsets, max_rows, E, I, d, d, w_down,
                                                               sc->out, s, sc->row_token, sc->T, nullptr, nullptr, 1,
-                                                              tail_ws, dn_sched, sc->row_w);
+                                                              tail_ws, dn_sched, sc->row_w, wtiled);
   else
     e = launch_auto<kEpiPlain, false>(h, expert_offsets, max_rows, E, I, d, d, w_down, y_perm, s, nullptr, 0,
-                                      nullptr, nullptr, dn_sched, tail_ws, !scatter_tiles);
+                                      nullptr, nullptr, dn_sched, tail_ws, !scatter_tiles, wtiled);
   if (e != hipSuccess || tail_ws == nullptr) return e;
   k_tail_sum<<<dim3(kTailPieces / 2, 288 / kTailSumRows), 256, 0, s>>>(
       tail_ws, d, sc ? sc->out : y_perm, sc ? sc->row_token : nullptr, sc ? sc->row_w : nullptr, sc ? sc->T : 0);
@@ -1559,6 +1582,50 @@ hipError_t launch_gate_up_dgrad_bf16(const bf16_t* dgu, const int32_t* expert_of
   return launch_auto<kEpiPlain, true>(dgu, expert_offsets, max_rows, E, 2 * I, d, 2 * I, w_gate_up, dx_perm, s);
 }
 
+// ---- column-tiled weights -------------------------------------------------
+// One expert's [K][ldw] weight as the products' column tiles read it: block
+// c (c = 0, 1, ...) holds the tile's columns as [K][width], width = the
+// tile's weight columns, blocks in column order; for gate/up (ldw = 2N) a
+// tile is TC gate columns n0 .. n0 + w - 1 and the same up columns, stored
+// gate first (width 2w), for down (ldw = N) TC columns (width w).  Every
+// block but the last is full, so block c starts at element K * c * TC
+// (gate/up: K * 2 c * TC).  One wave copies one row of one block, 16 bytes
+// a lane.
+__global__ __launch_bounds__(256) void k_tile_weights(const bf16_t* __restrict__ w, int E, int K, int N, int tc,
+                                                      bool gate_up, bf16_t* __restrict__ out) {
+  const int lane = threadIdx.x % kWave;
+  const int nb = (int)ceil_div(N, tc);
+  const int64_t rows = (int64_t)E * nb * K;
+  const int ldw = gate_up ? 2 * N : N;
+  for (int64_t q = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave; q < rows;
+       q += (int64_t)gridDim.x * (256 / kWave)) {
+    const int e = (int)(q / ((int64_t)nb * K));
+    const int c = (int)(q / K % nb);
+    const int k = (int)(q % K);
+    const int n0 = c * tc, wc = min(tc, N - n0);
+    const int width = gate_up ? 2 * wc : wc;
+    const bf16_t* src = w + ((int64_t)e * K + k) * ldw;
+    bf16_t* dst = out + (int64_t)e * K * ldw + (int64_t)K * (gate_up ? 2 * n0 : n0) + (int64_t)k * width;
+    for (int v = lane * 8; v < width; v += kWave * 8) {
+      // (wc is a multiple of 8: a vector never straddles the gate and up halves)
+      const int col = (gate_up && v >= wc) ? N + n0 + (v - wc) : n0 + v;
+      *(uint4*)(dst + v) = *(const uint4*)(src + col);
+    }
+  }
+}
+
+hipError_t launch_tile_weights_bf16(const bf16_t* w_gate_up, const bf16_t* w_down, int E, int d, int I,
+                                    bf16_t* wgu_tiled, bf16_t* wd_tiled, hipStream_t s) {
+  const int64_t rows_gu = (int64_t)E * ceil_div(I, kTileGateCols) * d;
+  const int64_t rows_dn = (int64_t)E * ceil_div(d, kTileDownCols) * I;
+  const unsigned cap = 65535u * 4u;
+  k_tile_weights<<<(unsigned)std::min<int64_t>(ceil_div(rows_gu, 4), cap), 256, 0, s>>>(w_gate_up, E, d, I,
+                                                                                       kTileGateCols, true, wgu_tiled);
+  k_tile_weights<<<(unsigned)std::min<int64_t>(ceil_div(rows_dn, 4), cap), 256, 0, s>>>(w_down, E, I, d,
+                                                                                       kTileDownCols, false, wd_tiled);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
                               int d, int I, const float* w_gate_up, float* h, hipStream_t s) {
   dim3 g((unsigned)max_rows, (unsigned)ceil_div(I, 256));
@@ -1575,11 +1642,13 @@ hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_
 
 hipError_t launch_grouped_ffn_bf16(const bf16_t* x_perm, const int32_t* expert_offsets, int64_t max_rows,
                                    int E, int d, int I, const bf16_t* w_gate_up, const bf16_t* w_down,
-                                   bf16_t* h, bf16_t* y_perm, hipStream_t s, float* split_ws, int32_t* sched) {
+                                   bf16_t* h, bf16_t* y_perm, hipStream_t s, float* split_ws, int32_t* sched,
+                                   bool wtiled) {
   const hipError_t e =
-      launch_gate_up_bf16(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s, nullptr, 0, sched);
+      launch_gate_up_bf16(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s, nullptr, 0, sched, wtiled);
   if (e != hipSuccess) return e;
-  return launch_down_bf16(h, expert_offsets, max_rows, E, d, I, w_down, y_perm, s, split_ws, sched);
+  return launch_down_bf16(h, expert_offsets, max_rows, E, d, I, w_down, y_perm, s, split_ws, sched, nullptr, false,
+                          wtiled);
 }
 
 hipError_t launch_grouped_ffn_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
