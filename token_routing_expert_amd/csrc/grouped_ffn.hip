@@ -228,7 +228,8 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   constexpr int XR = TALL ? 32 : 0;
   constexpr int A_STAGE = GE::A_BYTES + XR * BK * 2;  // LDS bytes of an activation stage
   typedef Geo<2 * BK, NJ, WM> GD;  // the activation geometry of a double-stage
-  // Activation double-stages (the ping-pong products with [K][N] weights):
+  // Activation double-stages (every ping-pong product; the backward's
+  // weights read as [N][K] rows keep single stages):
   // the activation rows of two consecutive k-stages arrive together, 128
   // bytes of a row per load lane group (8 rows per DMA instruction), in a
   // ring of two double-stages beside the four-stage weight ring.  A load
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(128 * WM, (OCC * WM + 1) / 2) void k_grouped_gemm(
   // requests for the same bytes, and the number of requests a CU can have
   // in flight is what paces these loads.  The activation loads of stages
   // g, g + 1 (g even) are issued with the weight loads of stage g + 1.
-  constexpr bool AD = PP && !BT;
+  constexpr bool AD = PP;
   static_assert(!AD || (BK == 32 && NS == 4 && WAVES == 8), "double-stages: 32-wide stages, a ring of four");
   constexpr int AD_ROW = 4 * BK;                    // bytes of a row in a double-stage
   constexpr int A_DSTAGE = (BM + XR) * AD_ROW;      // LDS bytes of a double-stage
