@@ -336,7 +336,7 @@ def roofline_of(inp, kernels, work, peak_mm, workload):
     if rec is not None and rec.get("source_sha256_16") == kernel_source_hash():
         traffic = float(rec["hbm_bytes_per_launch"])
     kernel = ("gate/up grouped GEMM + SwiGLU (dma::k_grouped_gemm<1, false, ...>, tile shape chosen per call)"
-              if inp.dtype == "bf16" else "gate/up grouped FFN (k_ffn_gate_up_f32)")
+              if inp.dtype == "bf16" else "gate/up grouped GEMM + SwiGLU, float32 MFMA (k_grouped_gemm_f32<true>)")
     common = {"kernel": kernel, "traffic": traffic, "flops_per_launch": w["flops"], "bytes_per_launch": w["bytes"],
               "arithmetic_intensity": round(ai, 1), "ridge": round(ridge, 1), "launch_ms": gu["ms"]}
     if ai < ridge:

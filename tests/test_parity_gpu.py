@@ -272,6 +272,7 @@ def check_grouped_ffn(tre, inp, idx):
     (520, 128, 2, 2, 256, "bf16"),    # an expert with several row tiles
     (64, 128, 8, 2, 256, "f32"),
     (77, 64, 6, 3, 64, "f32"),
+    (600, 192, 5, 2, 320, "f32"),     # float32 tiles: ragged 64-row tiles, a half down column tile (192 = 128 + 64)
     (40, 320, 6, 2, 2048, "bf16"),    # few rows: the down projection's k-stages split in ranges
 ])
 def test_grouped_ffn_random(tre, T, d, E, k, I, dtype):
@@ -330,8 +331,9 @@ def test_forward_split_tail_one_pair_per_token(tre):
     check_forward(tre, inp)
 
 
-def test_grouped_ffn_empty_experts(tre):
-    inp = workloads.make_custom(T=200, d=128, E=16, k=2, I=128, dtype="bf16", seed=5, logits="normal")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_grouped_ffn_empty_experts(tre, dtype):
+    inp = workloads.make_custom(T=200, d=128, E=16, k=2, I=128, dtype=dtype, seed=5, logits="normal")
     idx = np.where(np.arange(400).reshape(200, 2) % 2 == 0, 3, 11).astype(np.int32)   # only experts 3, 11
     check_grouped_ffn(tre, inp, idx)
 
@@ -666,6 +668,7 @@ def test_forward_tall_and_split_tail_shapes(tre, T, d, E, k, I, logits, want):
     (130, 128, 4, 4, 192, "bf16", "normal"),         # k = E
     (257, 64, 3, 2, 64, "f32", "uniform"),
     (1500, 64, 6, 2, 128, "f32", "normal"),          # float32 layer past the one-workgroup grouping
+    (700, 256, 9, 3, 448, "f32", "normal_bias"),     # float32: skewed experts, 7 gate/up and 2 down column tiles
     (1000, 192, 7, 3, 320, "bf16", "normal_bias"),
     (48, 256, 8, 2, 2048, "bf16", "normal"),         # few rows: k-split down projection
     (3, 64, 2, 1, 1024, "bf16", "normal"),           # a split over two ranges, one row per expert

@@ -42,8 +42,8 @@
 //     last round and a half is handed out by an atomic ticket counter;
 //   * with one pair per token the down projection can write the layer
 //     output rows itself (routing weight applied, as the combine would).
-// float32 path: plain per-element dot products (small, for the float32
-// workloads).
+// float32 path (v_mfma_f32_32x32x2_f32): 64 x 128 tiles of four waves,
+// double-buffered k-stages staged through registers into LDS.
 #include "common.hpp"
 
 #include <algorithm>
@@ -1263,48 +1263,126 @@ int persistent_grid(int64_t max_rows, int E, int bm, int n_tiles, int occ) {
 }
 
 // ---- float32 path -----------------------------------------------------------
+// Tiles of 64 grouped rows x 128 weight columns in k-stages of 32, four waves
+// (2 x 2) of 32 rows x 64 columns, each two 32 x 32 blocks of
+// v_mfma_f32_32x32x2_f32.  That MFMA takes A (32 x 2) with A[i][k] in lane
+// i + 32 k and B (2 x 32) with B[k][j] in lane j + 32 k, and register q of
+// lane l of its 32 x 32 float32 result holds row 8 (q / 4) + 4 (l / 32) +
+// q % 4, column l % 32.  A gate/up tile takes 64 gate columns and the
+// matching 64 up columns, and a wave's two blocks are gate columns j and up
+// columns j, so each SwiGLU pair meets in one lane and register.  Stages are
+// double-buffered in LDS: the next stage's global loads are in registers
+// while the current one is multiplied, and one barrier a stage separates
+// the two.  One workgroup per (row tile, column tile); row tiles are
+// numbered expert by expert from the device offsets, and the rows of a
+// tile's last partial block load as zeros and are not stored.
+constexpr int kF32Rows = 64, kF32Cols = 128, kF32K = 32;
 
-__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int64_t r) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restrict__ A,
+                                                          const int32_t* __restrict__ offsets, int64_t max_rows,
+                                                          int E, int K, int N, const float* __restrict__ W,
+                                                          float* __restrict__ Out) {
+  constexpr int BM = kF32Rows, BN = kF32Cols, BK = kF32K;
+  constexpr int LDA = BK + 1;   // a row of A in LDS (the pad spreads a wave's rows over the banks)
+  constexpr int LDB = BN + 32;  // a k-row of B in LDS (the pad puts k and k + 1 on different banks)
+  __shared__ float sA[2][BM * LDA];
+  __shared__ __attribute__((aligned(16))) float sB[2][BK * LDB];
+  __shared__ int s_wave[4];
+  __shared__ int s_tile[3];  // expert, first grouped row, rows
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+
+  // this workgroup's row tile
+  int mt = 0, lo = 0, cnt = 0;
+  if (tid < E) {
+    MOE_DCHECK(0 <= offsets[tid] && offsets[tid] <= offsets[tid + 1] && offsets[tid + 1] <= max_rows);
+    lo = (int)clampi<int64_t>(offsets[tid], 0, max_rows);
+    cnt = (int)clampi<int64_t>(offsets[tid + 1], lo, max_rows) - lo;
+    mt = (int)ceil_div(cnt, BM);
   }
-  return lo;
-}
-
-__global__ __launch_bounds__(256) void k_ffn_gate_up_f32(const float* __restrict__ x, const int32_t* __restrict__ offsets,
-                                                         int64_t max_rows, int E, int d, int I,
-                                                         const float* __restrict__ wgu, float* __restrict__ h) {
-  const int64_t r = blockIdx.x;
-  const int c = blockIdx.y * blockDim.x + threadIdx.x;
-  const int64_t n_rows = clampi<int64_t>(offsets[E], 0, max_rows);
-  if (r >= n_rows || c >= I) return;
-  const int e = expert_of_row(offsets, E, r);
-  const float* xr = x + r * d;
-  const float* we = wgu + (int64_t)e * d * 2 * I;
-  float g = 0.f, u = 0.f;
-  for (int q = 0; q < d; ++q) {
-    const float xv = xr[q];
-    g = fmaf(xv, we[(int64_t)q * 2 * I + c], g);
-    u = fmaf(xv, we[(int64_t)q * 2 * I + I + c], u);
+  int total = 0;
+  const int before = block_exclusive_scan<4>(mt, s_wave, &total);
+  const int u = (int)blockIdx.x;
+  if (u >= total) return;  // (the same for the whole workgroup)
+  if (tid < E && before <= u && u < before + mt) {
+    s_tile[0] = tid;
+    s_tile[1] = lo + (u - before) * BM;
+    s_tile[2] = min(BM, cnt - (u - before) * BM);
   }
-  h[r * I + c] = g / (1.f + expf(-g)) * u;
-}
+  __syncthreads();
+  const int e = s_tile[0], r0 = s_tile[1], rows = s_tile[2];
+  const int ldw = SWIGLU ? 2 * N : N;
+  const int n0 = (int)blockIdx.y * (SWIGLU ? BN / 2 : BN);
+  const float* We = W + (int64_t)e * K * ldw;
 
-__global__ __launch_bounds__(256) void k_ffn_down_f32(const float* __restrict__ h, const int32_t* __restrict__ offsets,
-                                                      int64_t max_rows, int E, int d, int I,
-                                                      const float* __restrict__ wd, float* __restrict__ y) {
-  const int64_t r = blockIdx.x;
-  const int c = blockIdx.y * blockDim.x + threadIdx.x;
-  const int64_t n_rows = clampi<int64_t>(offsets[E], 0, max_rows);
-  if (r >= n_rows || c >= d) return;
-  const int e = expert_of_row(offsets, E, r);
-  const float* hr = h + r * I;
-  const float* we = wd + (int64_t)e * I * d;
-  float acc = 0.f;
-  for (int q = 0; q < I; ++q) acc = fmaf(hr[q], we[(int64_t)q * d + c], acc);
-  y[r * d + c] = acc;
+  // the global column of LDS column cb (a multiple of 4), or -1 past N
+  auto gcol = [&](int cb) -> int {
+    if (SWIGLU) return cb < BN / 2 ? n0 + cb : N + n0 + cb - BN / 2;
+    return n0 + cb < N ? n0 + cb : -1;
+  };
+  f32x4 ra[2], rb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i, row = q / 8, c = 4 * (q % 8);
+      ra[i] = row < rows ? *(const f32x4*)(A + (int64_t)(r0 + row) * K + k0 + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, k = q / 32, col = gcol(4 * (q % 32));
+      rb[i] = col >= 0 ? *(const f32x4*)(We + (int64_t)(k0 + k) * ldw + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i, row = q / 8, c = 4 * (q % 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sA[buf][row * LDA + c + j] = ra[i][j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      *(f32x4*)&sB[buf][(q / 32) * LDB + 4 * (q % 32)] = rb[i];
+    }
+  };
+  // a wave's two column blocks in LDS
+  const int cb0 = SWIGLU ? 32 * wn : 64 * wn, cb1 = SWIGLU ? BN / 2 + 32 * wn : 64 * wn + 32;
+  f32x16 acc0 = {}, acc1 = {};
+  const int nk = K / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nk) load((s + 1) * BK);
+    const float* a = &sA[buf][(32 * wm + lane % 32) * LDA + lane / 32];
+    const float* b = &sB[buf][(lane / 32) * LDB + lane % 32];
+#pragma unroll
+    for (int kk = 0; kk < BK / 2; ++kk) {
+      const float av = a[2 * kk];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[2 * kk * LDB + cb0], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[2 * kk * LDB + cb1], acc1, 0, 0, 0);
+    }
+    if (s + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+  // epilogue: register q of this lane is row 8 (q / 4) + 4 (lane / 32) + q % 4 of the wave's 32 rows
+  const int col = lane % 32;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int r = 32 * wm + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
+    if (r >= rows) continue;
+    float* o = Out + (int64_t)(r0 + r) * N;
+    if (SWIGLU) {
+      const float g = acc0[q], up = acc1[q];
+      o[n0 + 32 * wn + col] = g / (1.f + expf(-g)) * up;
+    } else {
+      if (n0 + cb0 + col < N) o[n0 + cb0 + col] = acc0[q];
+      if (n0 + cb1 + col < N) o[n0 + cb1 + col] = acc1[q];
+    }
+  }
 }
 
 template <int EPI, bool BT = false, int BK = 32, int OCC = 2, int NJ = 4, int WM = 2, int NS = 3, bool PP = false,
@@ -1627,17 +1705,24 @@ hipError_t launch_tile_weights_bf16(const bf16_t* w_gate_up, const bf16_t* w_dow
   return hipGetLastError();
 }
 
+// row tiles a float32 launch may need: ceil(rows_e / 64) summed over the experts
+static unsigned f32_row_tiles(int64_t max_rows, int E) {
+  return (unsigned)(max_rows / kF32Rows + (E < max_rows ? E : max_rows));
+}
+
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
                               int d, int I, const float* w_gate_up, float* h, hipStream_t s) {
-  dim3 g((unsigned)max_rows, (unsigned)ceil_div(I, 256));
-  k_ffn_gate_up_f32<<<g, 256, 0, s>>>(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h);
+  const dim3 g(f32_row_tiles(max_rows, E), (unsigned)ceil_div(I, kF32Cols / 2));
+  if (g.x == 0 || g.y == 0) return hipSuccess;
+  k_grouped_gemm_f32<true><<<g, 256, 0, s>>>(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h);
   return hipGetLastError();
 }
 
 hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                            int I, const float* w_down, float* y_perm, hipStream_t s) {
-  dim3 g((unsigned)max_rows, (unsigned)ceil_div(d, 256));
-  k_ffn_down_f32<<<g, 256, 0, s>>>(h, expert_offsets, max_rows, E, d, I, w_down, y_perm);
+  const dim3 g(f32_row_tiles(max_rows, E), (unsigned)ceil_div(d, kF32Cols));
+  if (g.x == 0 || g.y == 0) return hipSuccess;
+  k_grouped_gemm_f32<false><<<g, 256, 0, s>>>(h, expert_offsets, max_rows, E, I, d, w_down, y_perm);
   return hipGetLastError();
 }
 
