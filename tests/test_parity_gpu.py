@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 import workloads
-from helpers import TOL, as_f64, check_outputs, rel_l2, to_device, to_host
+from helpers import PARITY_LOG, TOL, as_f64, check_outputs, rel_l2, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -967,12 +967,15 @@ def check_backward(tre, inp, seed):
         errs[key] = rel_l2(got[key], r)
         if key == "dx":
             # every token's row on its own as well
-            _, worst, _ = check_outputs(got[key], r, TOL["bf16"])
+            _, worst, _ = check_outputs(got[key], r, TOL["bf16"], label=f"backward {inp.name} dx")
             errs["dx worst row"] = worst
         elif key.startswith("dw_"):
             # every expert's weight gradient on its own as well
-            per = [rel_l2(got[key][e], r[e]) for e in range(inp.E) if np.any(r[e])]
-            errs[key + " worst expert"] = max(per)
+            per = {e: rel_l2(got[key][e], r[e]) for e in range(inp.E) if np.any(r[e])}
+            worst_e = max(per, key=per.get)
+            errs[key + " worst expert"] = per[worst_e]
+            PARITY_LOG.append((f"backward {inp.name} {key} (rows: experts)", errs[key], per[worst_e], worst_e,
+                               inp.E, TOL["bf16"]))
     say(f"  backward {inp.name} T={inp.T} d={inp.d} E={inp.E} k={inp.k} I={inp.I}: " +
         ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     for key, v in errs.items():
@@ -1020,6 +1023,15 @@ def test_backward_ep_rank_share(tre):
     inp = workload("ep_rank_share")
     say("backward ep_rank_share (full oracle)")
     check_backward(tre, inp, seed=68)
+
+
+def test_backward_large_e128(tre):
+    # the 128-expert layer at full size: 8192 tokens routed by their logits
+    # (k = 4, so the logit gradient too), every token's dx row, every
+    # expert's weight gradients
+    inp = workload("large_e128")
+    say("backward large_e128 (full oracle)")
+    check_backward(tre, inp, seed=69)
 
 
 def test_backward_deterministic(tre):
