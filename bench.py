@@ -529,9 +529,10 @@ def main() -> int:
         # moe_backward, which recomputes the forward it needs, and a training
         # step (the forward that keeps its intermediates, then the backward
         # from them) ----
-        if "backward" in extras and inp.dtype == "bf16":
+        if "backward" in extras:
             rng = np.random.default_rng([inp_seed(args.workload), 99])
-            dout = to_device(workloads.bf16_bits(rng.normal(size=(T, d)).astype(np.float32)), torch)
+            g32 = rng.normal(size=(T, d)).astype(np.float32)
+            dout = to_device(g32 if inp.dtype == "f32" else workloads.bf16_bits(g32), torch)
             gdx = torch.empty((T, d), dtype=dev_dtype, device="cuda")
             gwgu = torch.empty((E, d, 2 * I), dtype=dev_dtype, device="cuda")
             gwd = torch.empty((E, I, d), dtype=dev_dtype, device="cuda")
@@ -570,7 +571,8 @@ def main() -> int:
             b_flops = 18 * n_rows * d * I
             backward = {"ms": round(b_ms, 5), "flops_per_call": b_flops,
                         "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 1),
-                        "mfma_frac": round(b_flops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "mfma_frac": round(b_flops / (b_ms * 1e-3) / 1e12 /
+                                           (PEAK_F32_TFLOPS if inp.dtype == "f32" else PEAK_BF16_TFLOPS), 4),
                         "pairs_per_s": P / (b_ms * 1e-3),
                         # training step: 6 n d I (forward) + 12 n d I (gradients), no recompute
                         "training_step": {"ms": round(step_ms, 5), "forward_train_ms": round(ft_ms, 5),

@@ -245,19 +245,20 @@ moe_status moe_forward_noalloc(const void* x, const float* logits, int32_t T, in
  * given, the grouping, both projections).  recompute = 0: the workspace
  * holds what moe_forward_train left there for these same arguments (and
  * topk_idx / topk_w are the arrays that call filled or read), untouched since;
- * only the gradients are computed.  bf16 only: bf16 operands and stored
+ * only the gradients are computed.  dt = MOE_BF16: bf16 operands and stored
  * intermediates (the pre-activations g, u, h, y and the row gradients),
- * float32 accumulation, gradients rounded to bf16 (dtopk_w, dlogits float32).
- *   x, dout [T, d] bf16; w_gate_up [E, d, 2I], w_down [E, I, d] bf16
+ * float32 accumulation, gradients rounded to bf16; dt = MOE_F32: float32
+ * throughout (dtopk_w and dlogits are float32 for both).
+ *   x, dout [T, d] dt; w_gate_up [E, d, 2I], w_down [E, I, d] dt
  *   logits [T, E] float32 or NULL, and topk_idx / topk_w [T, k], as for
  *     moe_forward (outputs with logits, inputs without; -1 ids are skipped)
- *   dx [T, d], dw_gate_up [E, d, 2I], dw_down [E, I, d] bf16 (outputs,
+ *   dx [T, d], dw_gate_up [E, d, 2I], dw_down [E, I, d] dt (outputs,
  *     overwritten); dtopk_w [T, k] float32 (output, 0 for skipped pairs);
  *     dlogits [T, E] float32 (output; NULL to skip; only with logits)
  *   workspace >= moe_backward_workspace_size(T, d, E, k, I, dt) bytes
- * Errors: as moe_forward; MOE_ERR_UNSUPPORTED for dt = MOE_F32; MOE_ERR_ARG
- * for dlogits without logits or recompute not 0 or 1.  T == 0 zeroes the
- * weight gradients only.                                                    */
+ *     (the size depends on dt; 0 for an unknown dt)
+ * Errors: as moe_forward; MOE_ERR_ARG for dlogits without logits or
+ * recompute not 0 or 1.  T == 0 zeroes the weight gradients only.          */
 size_t moe_backward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, moe_dtype dt);
 moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k,
                         int32_t I, const void* w_gate_up, const void* w_down, moe_dtype dt,
@@ -269,7 +270,7 @@ moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d
  * (same kernels, same order of every sum), and the intermediates the
  * backward needs -- the routing, the grouping, the grouped rows of x, the
  * pre-activations g | u, h and the expert outputs y -- kept in the workspace
- * for moe_backward(..., recompute = 0, same workspace).  bf16 only.
+ * for moe_backward(..., recompute = 0, same workspace).  bf16 or float32.
  *   arguments as moe_forward (the expert_offsets / row_token / pair_row
  *   outputs live in the workspace);
  *   workspace >= moe_backward_workspace_size(T, d, E, k, I, dt) bytes        */

@@ -135,7 +135,7 @@ def test_backward_validation(lib):
              ws_bytes=0, recompute=1):
         return f(x, logits, T, d, E, k, I, FAKE, FAKE, dt, FAKE, FAKE, dout, FAKE, FAKE, FAKE, FAKE, dlogits,
                  recompute, ws, ws_bytes, None)
-    assert call(dt=0) == 2                    # float32: not supported
+    assert call(dt=0) == 3                    # float32: supported, and the workspace is too small
     assert call(dt=5) == 1                    # bad dtype
     assert call(k=9) == 1                     # k > E with logits
     assert call(E=300) == 2                   # E > 256
@@ -148,7 +148,9 @@ def test_backward_validation(lib):
     assert call(recompute=2) == 1             # recompute is 0 or 1
     need = lib.moe_backward_workspace_size(10, 128, 8, 2, 64, 1)
     assert call(ws=None, ws_bytes=need) == 3  # no workspace
-    assert lib.moe_backward_workspace_size(10, 128, 8, 2, 64, 0) == 0
+    # float32: its seven row buffers (x, y, dy, dx rows; h; g | u and their gradient), 4 bytes an element
+    assert lib.moe_backward_workspace_size(10, 128, 8, 2, 64, 0) >= 20 * 4 * (4 * 128 + 64 + 2 * 2 * 64)
+    assert lib.moe_backward_workspace_size(10, 128, 8, 2, 64, 7) == 0      # no such dtype
     assert need > lib.moe_forward_workspace_size(10, 128, 8, 2, 64, 1)
     assert lib.moe_backward_workspace_size(20, 128, 8, 2, 64, 1) > need
 
@@ -163,7 +165,8 @@ def test_forward_train_validation(lib):
 
     def call(x=FAKE, logits=FAKE, T=10, d=128, E=8, k=2, I=64, dt=1, out=FAKE, ws=FAKE, ws_bytes=0):
         return f(x, logits, T, d, E, k, I, FAKE, FAKE, dt, FAKE, FAKE, out, ws, ws_bytes, None)
-    assert call(dt=0) == 2                    # float32: not supported
+    assert call(dt=0) == 3                    # float32: supported, and the workspace is too small
+    assert call(dt=5) == 1                    # bad dtype
     assert call(k=9) == 1                     # k > E with logits
     assert call(d=96) == 2                    # d % 64
     assert call(out=None) == 1

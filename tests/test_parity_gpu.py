@@ -943,9 +943,15 @@ def run_backward(tre, inp, dout_bits):
     return {key: to_host(v) for key, v in res.items()}
 
 
+def upstream_grad(inp, seed):
+    """A seeded N(0, 1) upstream gradient in the layer's element type."""
+    g = np.random.default_rng(seed).normal(size=(inp.T, inp.d)).astype(np.float32)
+    return g if inp.dtype == "f32" else workloads.bf16_bits(g)
+
+
 def check_backward(tre, inp, seed):
-    rng = np.random.default_rng(seed)
-    dout = workloads.bf16_bits(rng.normal(size=(inp.T, inp.d)).astype(np.float32))
+    dout = upstream_grad(inp, seed)
+    tol = TOL[inp.dtype]
     got = run_backward(tre, inp, dout)
     d64 = workloads.to_float32(dout).astype(np.float64)
     if inp.logits is not None:
@@ -967,7 +973,7 @@ def check_backward(tre, inp, seed):
         errs[key] = rel_l2(got[key], r)
         if key == "dx":
             # every token's row on its own as well
-            _, worst, _ = check_outputs(got[key], r, TOL["bf16"], label=f"backward {inp.name} dx")
+            _, worst, _ = check_outputs(got[key], r, tol, label=f"backward {inp.name} dx")
             errs["dx worst row"] = worst
         elif key.startswith("dw_"):
             # every expert's weight gradient on its own as well
@@ -975,11 +981,11 @@ def check_backward(tre, inp, seed):
             worst_e = max(per, key=per.get)
             errs[key + " worst expert"] = per[worst_e]
             PARITY_LOG.append((f"backward {inp.name} {key} (rows: experts)", errs[key], per[worst_e], worst_e,
-                               inp.E, TOL["bf16"]))
+                               inp.E, tol))
     say(f"  backward {inp.name} T={inp.T} d={inp.d} E={inp.E} k={inp.k} I={inp.I}: " +
         ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     for key, v in errs.items():
-        assert v <= TOL["bf16"], key
+        assert v <= tol, key
     # experts that received no rows have exactly zero weight gradients
     ids = ref["idx"].reshape(-1)
     for e in range(inp.E):
@@ -1003,8 +1009,28 @@ def test_backward_shapes(tre, T, d, E, k, I, logits):
         assert not np.any(got["dlogits"])
 
 
-def test_backward_given_pairs_with_masked(tre):
-    inp = workloads.make_custom(T=600, d=128, E=16, k=1, I=128, dtype="bf16", seed=63, logits=None,
+@pytest.mark.parametrize("T,d,E,k,I,logits", [
+    (300, 256, 8, 2, 320, "normal"),
+    (1000, 192, 7, 3, 320, "normal_bias"),   # ragged experts, a half column tile of dW_down (192 = 128 + 64)
+    (64, 128, 16, 1, 128, "normal"),         # k = 1: no logit gradient
+    (5, 64, 256, 8, 64, "normal"),           # most experts empty, widest E
+])
+def test_backward_shapes_f32(tre, T, d, E, k, I, logits):
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="f32", seed=T + E + 150, logits=logits)
+    got, _ = check_backward(tre, inp, seed=T + 1)
+    if k == 1:
+        assert not np.any(got["dlogits"])
+
+
+def test_backward_tiny_f32(tre):
+    # the float32 workload's layer (router logits from the router projection, k = 2)
+    inp = workload("tiny_f32")
+    check_backward(tre, inp, seed=70)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_given_pairs_with_masked(tre, dtype):
+    inp = workloads.make_custom(T=600, d=128, E=16, k=1, I=128, dtype=dtype, seed=63, logits=None,
                                 zero_experts=3)
     inp.pair_expert[::9] = -1
     got, _ = check_backward(tre, inp, seed=64)
@@ -1034,43 +1060,48 @@ def test_backward_large_e128(tre):
     check_backward(tre, inp, seed=69)
 
 
-def test_backward_deterministic(tre):
-    inp = workloads.make_custom(T=512, d=256, E=8, k=2, I=256, dtype="bf16", seed=66, logits="normal")
-    dout = workloads.bf16_bits(np.random.default_rng(67).normal(size=(512, 256)).astype(np.float32))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_deterministic(tre, dtype):
+    inp = workloads.make_custom(T=512, d=256, E=8, k=2, I=256, dtype=dtype, seed=66, logits="normal")
+    dout = upstream_grad(inp, 67)
     a = run_backward(tre, inp, dout)
     b = run_backward(tre, inp, dout)
     for key in a:
         assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
 
 
-def test_backward_empty_batch(tre):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_empty_batch(tre, dtype):
     torch = _torch()
-    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
-    wgu = torch.ones((4, 128, 256), dtype=torch.bfloat16, device="cuda")
-    wd = torch.ones((4, 128, 128), dtype=torch.bfloat16, device="cuda")
-    res = tre.moe_backward(x, wgu, wd, 2, torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda"),
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.zeros((0, 128), dtype=dt, device="cuda")
+    wgu = torch.ones((4, 128, 256), dtype=dt, device="cuda")
+    wd = torch.ones((4, 128, 128), dtype=dt, device="cuda")
+    res = tre.moe_backward(x, wgu, wd, 2, torch.zeros((0, 128), dtype=dt, device="cuda"),
                            logits=torch.zeros((0, 4), dtype=torch.float32, device="cuda"))
     sync()
     assert not torch.any(res["dw_gate_up"].float()) and not torch.any(res["dw_down"].float())
 
 
-@pytest.mark.parametrize("T,d,E,k,I,logits", [
-    (300, 256, 8, 2, 320, "normal"),
-    (4096, 512, 8, 2, 576, "normal_bias"),   # 256-row tiles
-    (600, 128, 16, 1, 128, None),            # given pairs, some masked
-    (48, 256, 8, 2, 2048, "normal"),         # few rows: k-split down projection in both forwards
-    (16384, 1024, 64, 1, 512, "normal"),     # one pair per token, ~256 rows an expert: a split tail in both
+@pytest.mark.parametrize("T,d,E,k,I,logits,dtype", [
+    (300, 256, 8, 2, 320, "normal", "bf16"),
+    (4096, 512, 8, 2, 576, "normal_bias", "bf16"),   # 256-row tiles
+    (600, 128, 16, 1, 128, None, "bf16"),            # given pairs, some masked
+    (48, 256, 8, 2, 2048, "normal", "bf16"),         # few rows: k-split down projection in both forwards
+    (16384, 1024, 64, 1, 512, "normal", "bf16"),     # one pair per token, ~256 rows an expert: a split tail in both
+    (300, 256, 8, 2, 320, "normal", "f32"),
+    (600, 128, 16, 1, 128, None, "f32"),             # float32, given pairs, some masked
 ])
-def test_training_step_saved_equals_recompute(tre, T, d, E, k, I, logits):
+def test_training_step_saved_equals_recompute(tre, T, d, E, k, I, logits, dtype):
     # the training forward's output equals moe_forward's bit for bit, and the
     # backward from its saved state equals the recomputing backward bit for bit
     torch = _torch()
-    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype="bf16", seed=T + 70, logits=logits,
+    inp = workloads.make_custom(T=T, d=d, E=E, k=k, I=I, dtype=dtype, seed=T + 70, logits=logits,
                                 zero_experts=3 if logits is None else 0)
     if logits is None:
         inp.pair_expert[::7] = -1
     x, wgu, wd = to_device(inp.x), to_device(inp.w_gate_up), to_device(inp.w_down)
-    dout = to_device(workloads.bf16_bits(np.random.default_rng(T).normal(size=(T, d)).astype(np.float32)))
+    dout = to_device(upstream_grad(inp, T))
     if logits is not None:
         lg = to_device(inp.logits)
         ref_out, ref_idx, ref_w = tre.moe_forward(x, wgu, wd, k, logits=lg)
@@ -1086,7 +1117,7 @@ def test_training_step_saved_equals_recompute(tre, T, d, E, k, I, logits):
         g_re = tre.moe_backward(x, wgu, wd, k, dout, topk_idx=pi, topk_w=pw)
         g_sv = tre.moe_backward(x, wgu, wd, k, dout, topk_idx=idx, topk_w=w, workspace=ws, recompute=False)
     sync()
-    assert np.array_equal(to_host(out).view(np.uint16), to_host(ref_out).view(np.uint16))
+    assert np.array_equal(to_host(out).view(np.uint8), to_host(ref_out).view(np.uint8))
     assert np.array_equal(to_host(idx), to_host(ref_idx))
     for key in g_re:
         assert np.array_equal(to_host(g_re[key]).view(np.uint8), to_host(g_sv[key]).view(np.uint8)), key
@@ -1094,7 +1125,7 @@ def test_training_step_saved_equals_recompute(tre, T, d, E, k, I, logits):
     ref = oracle.backward(inp.x, inp.w_gate_up, inp.w_down, k, workloads.to_float32(to_host(dout)).astype(np.float64),
                           logits=inp.logits, pair_expert=inp.pair_expert, pair_w=inp.pair_w)
     for key, rkey in (("dx", "dx"), ("dw_gate_up", "dw_gate_up"), ("dw_down", "dw_down"), ("dtopk_w", "dw")):
-        assert rel_l2(to_host(g_sv[key]), ref[rkey]) <= TOL["bf16"], key
+        assert rel_l2(to_host(g_sv[key]), ref[rkey]) <= TOL[dtype], key
 
 
 _DEBUG_LIB = []

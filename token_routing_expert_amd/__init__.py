@@ -410,7 +410,7 @@ def moe_backward_workspace_size(T: int, d: int, E: int, k: int, I: int, dtype) -
 
 def moe_forward_train(x, w_gate_up, w_down, k: int, logits=None, topk_idx=None, topk_w=None, out=None,
                       workspace=None, stream=None):
-    """The forward of a training step (bf16): ``out`` as moe_forward computes it, and
+    """The forward of a training step (bf16 or float32): ``out`` as moe_forward computes it, and
     the intermediates the backward needs kept in ``workspace`` (a backward-sized
     buffer, allocated when None).  Returns (out, topk_idx, topk_w, workspace); pass
     the same topk arrays and workspace to ``moe_backward(..., recompute=False)``."""
@@ -444,7 +444,7 @@ def moe_forward_train(x, w_gate_up, w_down, k: int, logits=None, topk_idx=None, 
 
 def moe_backward(x, w_gate_up, w_down, k: int, dout, logits=None, topk_idx=None, topk_w=None,
                  want_dlogits: bool = True, workspace=None, recompute: bool = True, stream=None):
-    """Gradients of <dout, moe_forward(x, ...)> (bf16).  With ``logits`` the layer
+    """Gradients of <dout, moe_forward(x, ...)> (bf16 or float32).  With ``logits`` the layer
     routes first (topk_idx / topk_w are outputs, and dlogits is returned when
     ``want_dlogits``); without, ``topk_idx`` / ``topk_w`` are the given pairs.
     ``recompute=False`` uses what moe_forward_train left in ``workspace`` (pass its

@@ -67,7 +67,9 @@ struct BackwardLayout {
   size_t pair_row, row_token, offsets, perm_ws, x_perm, h, gu, y, dy, dgu, dxp, split, sched, total;
 };
 
-BackwardLayout backward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I) {
+// s: bytes per element of the activation dtype (the float32 products split
+// no k-ranges, so their layout has no split workspace)
+BackwardLayout backward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64_t I, int64_t s) {
   const int64_t P = T * k;
   BackwardLayout L;
   size_t o = 0;
@@ -75,14 +77,14 @@ BackwardLayout backward_layout(int64_t T, int64_t d, int64_t E, int64_t k, int64
   L.row_token = o; o += align256(P * 4);
   L.offsets = o;   o += align256((E + 1) * 4);
   L.perm_ws = o;   o += permute_index_workspace(P, (int)E);
-  L.x_perm = o;    o += align256(P * d * 2);
-  L.h = o;         o += align256(P * I * 2);
-  L.gu = o;        o += align256(P * 2 * I * 2);
-  L.y = o;         o += align256(P * d * 2);
-  L.dy = o;        o += align256(P * d * 2);
-  L.dgu = o;       o += align256(P * 2 * I * 2);
-  L.dxp = o;       o += align256(P * d * 2);
-  L.split = o;     o += align256(split_workspace(P, (int)E, (int)d, (int)I));
+  L.x_perm = o;    o += align256(P * d * s);
+  L.h = o;         o += align256(P * I * s);
+  L.gu = o;        o += align256(P * 2 * I * s);
+  L.y = o;         o += align256(P * d * s);
+  L.dy = o;        o += align256(P * d * s);
+  L.dgu = o;       o += align256(P * 2 * I * s);
+  L.dxp = o;       o += align256(P * d * s);
+  L.split = o;     o += s == 2 ? align256(split_workspace(P, (int)E, (int)d, (int)I)) : 0;
   L.sched = o;     o += align256(kSchedWords * 4);
   L.total = o;
   return L;
@@ -416,16 +418,15 @@ moe_status moe_forward_noalloc(const void* x, const float* logits, int32_t T, in
 }
 
 size_t moe_backward_workspace_size(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, moe_dtype dt) {
-  if (T < 0 || d < 1 || E < 1 || k < 1 || I < 1 || dt != MOE_BF16) return 0;
-  return backward_layout(T, d, E, k, I).total;
+  if (T < 0 || d < 1 || E < 1 || k < 1 || I < 1 || !dtype_ok(dt)) return 0;
+  return backward_layout(T, d, E, k, I, elem_size(dt)).total;
 }
 
 namespace {
 
-// Validation shared by the training forward and the backward (bf16 only).
+// Validation shared by the training forward and the backward.
 moe_status check_train(moe_dtype dt, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, const float* logits) {
   if (!dtype_ok(dt) || T < 0 || k < 1) return MOE_ERR_ARG;
-  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   TRY(check_experts(E));
   if (logits && k > E) return MOE_ERR_ARG;
   TRY(check_width(d));
@@ -441,20 +442,26 @@ moe_status check_train(moe_dtype dt, int32_t T, int32_t d, int32_t E, int32_t k,
 // workspace: routing (with logits), grouping, the grouped copy of x, the
 // pre-activations g | u, h and the expert outputs y.
 moe_status forward_keep(const void* x, const float* logits, int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
-                        const void* w_gate_up, const void* w_down, int32_t* topk_idx, float* topk_w,
+                        const void* w_gate_up, const void* w_down, moe_dtype dt, int32_t* topk_idx, float* topk_w,
                         const BackwardLayout& L, char* ws, hipStream_t s) {
   const int64_t P = (int64_t)T * k;
   int32_t* p_row = (int32_t*)(ws + L.pair_row);
   int32_t* r_tok = (int32_t*)(ws + L.row_token);
   int32_t* offs = (int32_t*)(ws + L.offsets);
+  if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
+  int32_t* sched = (int32_t*)(ws + L.sched);
+  TRY(from_hip(launch_permute_rows(topk_idx, T, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched, x,
+                                   (int64_t)d * elem_size(dt), ws + L.x_perm)));
+  if (dt == MOE_F32) {
+    float* h = (float*)(ws + L.h);
+    TRY(from_hip(launch_gate_up_save_f32((const float*)(ws + L.x_perm), offs, P, E, d, I, (const float*)w_gate_up,
+                                         h, (float*)(ws + L.gu), s)));
+    return from_hip(launch_down_f32(h, offs, P, E, d, I, (const float*)w_down, (float*)(ws + L.y), s));
+  }
   bf16_t* x_perm = (bf16_t*)(ws + L.x_perm);
   bf16_t* h = (bf16_t*)(ws + L.h);
   bf16_t* gu = (bf16_t*)(ws + L.gu);
   bf16_t* y = (bf16_t*)(ws + L.y);
-  if (logits) TRY(from_hip(launch_route_topk(logits, T, E, k, topk_idx, topk_w, s)));
-  int32_t* sched = (int32_t*)(ws + L.sched);
-  TRY(from_hip(launch_permute_rows(topk_idx, T, k, E, r_tok, p_row, offs, ws + L.perm_ws, s, sched, x,
-                                   (int64_t)d * 2, x_perm)));
   TRY(from_hip(launch_gate_up_save_bf16(x_perm, offs, P, E, d, I, (const bf16_t*)w_gate_up, h, gu, s, nullptr, 0,
                                         sched)));
   // with one pair per token, moe_forward's down projection writes the output
@@ -473,11 +480,14 @@ moe_status moe_forward_train(const void* x, const float* logits, int32_t T, int3
   TRY(check_train(dt, T, d, E, k, I, logits));
   if (T == 0) return MOE_OK;
   if (!x || !w_gate_up || !w_down || !topk_idx || !topk_w || !out) return MOE_ERR_ARG;
-  const BackwardLayout L = backward_layout(T, d, E, k, I);
+  const BackwardLayout L = backward_layout(T, d, E, k, I, elem_size(dt));
   if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  TRY(forward_keep(x, logits, T, d, E, k, I, w_gate_up, w_down, topk_idx, topk_w, L, ws, s));
+  TRY(forward_keep(x, logits, T, d, E, k, I, w_gate_up, w_down, dt, topk_idx, topk_w, L, ws, s));
+  if (dt == MOE_F32)
+    return from_hip(launch_combine_f32((const float*)(ws + L.y), (int64_t)T * k, (const int32_t*)(ws + L.pair_row),
+                                       topk_w, T, k, d, (float*)out, s));
   return from_hip(launch_combine_bf16((const bf16_t*)(ws + L.y), (int64_t)T * k, (const int32_t*)(ws + L.pair_row),
                                       topk_w, T, k, d, (bf16_t*)out, s));
 }
@@ -491,15 +501,17 @@ moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d
   if (recompute != 0 && recompute != 1) return MOE_ERR_ARG;
   const int64_t P = (int64_t)T * k;
   if (T == 0) {
-    // no rows: every weight gradient is zero, and nothing else exists
+    // no rows: every weight gradient is zero, and nothing else exists (a
+    // float32 element is cleared as two bf16 ones)
     if (E > 0 && (!dw_gate_up || !dw_down)) return MOE_ERR_ARG;
     hipStream_t s0 = (hipStream_t)stream;
-    TRY(from_hip(launch_zero_bf16((bf16_t*)dw_gate_up, (int64_t)E * d * 2 * I, s0)));
-    return from_hip(launch_zero_bf16((bf16_t*)dw_down, (int64_t)E * I * d, s0));
+    const int64_t halves = dt == MOE_F32 ? 2 : 1;
+    TRY(from_hip(launch_zero_bf16((bf16_t*)dw_gate_up, (int64_t)E * d * 2 * I * halves, s0)));
+    return from_hip(launch_zero_bf16((bf16_t*)dw_down, (int64_t)E * I * d * halves, s0));
   }
   if (!x || !w_gate_up || !w_down || !topk_idx || !topk_w || !dout || !dx || !dw_gate_up || !dw_down || !dtopk_w)
     return MOE_ERR_ARG;
-  const BackwardLayout L = backward_layout(T, d, E, k, I);
+  const BackwardLayout L = backward_layout(T, d, E, k, I, elem_size(dt));
   if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
 
   char* ws = (char*)workspace;
@@ -519,7 +531,24 @@ moe_status moe_backward(const void* x, const float* logits, int32_t T, int32_t d
 
   // the forward again, keeping what the gradients need (or, without
   // recompute, what moe_forward_train left in this workspace)
-  if (recompute) TRY(forward_keep(x, logits, T, d, E, k, I, w_gate_up, w_down, topk_idx, topk_w, L, ws, s));
+  if (recompute) TRY(forward_keep(x, logits, T, d, E, k, I, w_gate_up, w_down, dt, topk_idx, topk_w, L, ws, s));
+  if (dt == MOE_F32) {
+    float* fh = (float*)(ws + L.h);
+    float* fgu = (float*)(ws + L.gu);
+    float* fdy = (float*)(ws + L.dy);
+    float* fdgu = (float*)(ws + L.dgu);
+    float* fdxp = (float*)(ws + L.dxp);
+    const float* fwgu = (const float*)w_gate_up;
+    const float* fwd = (const float*)w_down;
+    TRY(from_hip(launch_combine_bwd_f32((const float*)dout, (const float*)(ws + L.y), P, p_row, topk_w, topk_idx, T,
+                                        k, d, E, fdy, dtopk_w, dlogits, s)));
+    TRY(from_hip(launch_down_dgrad_swiglu_f32(fdy, offs, P, E, d, I, fwd, fgu, fdgu, s)));
+    TRY(from_hip(launch_wgrad_f32(fh, I, I, fdy, d, d, offs, P, E, (float*)dw_down, s)));
+    TRY(from_hip(launch_gate_up_dgrad_f32(fdgu, offs, P, E, d, I, fwgu, fdxp, s)));
+    TRY(from_hip(launch_wgrad_f32((const float*)(ws + L.x_perm), d, d, fdgu, 2 * I, 2 * I, offs, P, E,
+                                  (float*)dw_gate_up, s)));
+    return from_hip(launch_combine_f32(fdxp, P, p_row, nullptr, T, k, d, (float*)dx, s));
+  }
   // combine -> routing weights (and logits) and the expert rows' gradient
   TRY(from_hip(launch_combine_bwd_bf16((const bf16_t*)dout, y, P, p_row, topk_w, topk_idx, T, k, d, E, dy, dtopk_w,
                                        dlogits, s)));

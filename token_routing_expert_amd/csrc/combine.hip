@@ -140,13 +140,14 @@ __global__ __launch_bounds__(kThreads) void k_combine(const u32x4* __restrict__ 
   }
 }
 
-// Backward of the combine (bf16).  With dy_p = w_p dout_t for pair p = (t, j):
+// Backward of the combine.  With dy_p = w_p dout_t for pair p = (t, j):
 //   dy[pair_row[p]] = w_p * dout[t]          (the gradient reaching the expert)
 //   dw[p]           = <dout[t], y[pair_row[p]]>  (the routing weight's gradient)
 // and, when the weights are the softmax of the selected logits,
 //   dlogits[t, topk_idx[p]] = w_p (dw_p - sum_i w_i dw_i), zero elsewhere.
 // One wave per token, slots in ascending order; each dot product is summed
 // in float32 over the lanes' 16-byte vectors and then across the wave.
+template <typename Elem>
 __global__ __launch_bounds__(kThreads) void k_combine_bwd(
     const u32x4* __restrict__ dout, const u32x4* __restrict__ y, int64_t max_rows, const int32_t* __restrict__ pair_row,
     const float* __restrict__ pair_w, const int32_t* __restrict__ topk_idx, int64_t n_tok, int k, int E,
@@ -166,14 +167,15 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(
     float dot = 0.f;
     if (live) {
       for (int64_t v = lane; v < vec_per_row; v += kWave) {
-        float g[8], f[8];
-        Vec<bf16_t>::load(dout[t * vec_per_row + v], g);
-        Vec<bf16_t>::load(y[r * vec_per_row + v], f);
+        constexpr int NV = Vec<Elem>::n;
+        float g[NV], f[NV];
+        Vec<Elem>::load(dout[t * vec_per_row + v], g);
+        Vec<Elem>::load(y[r * vec_per_row + v], f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dot = fmaf(g[i], f[i], dot);
+        for (int i = 0; i < NV; ++i) dot = fmaf(g[i], f[i], dot);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) g[i] *= w;
-        dy[r * vec_per_row + v] = Vec<bf16_t>::store(g);
+        for (int i = 0; i < NV; ++i) g[i] *= w;
+        dy[r * vec_per_row + v] = Vec<Elem>::store(g);
       }
 #pragma unroll
       for (int off = kWave / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, kWave);
@@ -238,15 +240,32 @@ hipError_t launch_combine_bf16(const bf16_t* y_perm, int64_t max_rows, const int
   return launch<bf16_t>(y_perm, max_rows, pair_row, pair_w, T, k, d, out, s);
 }
 
+namespace {
+
+template <typename Elem>
+hipError_t launch_bwd(const Elem* dout, const Elem* y_perm, int64_t max_rows, const int32_t* pair_row,
+                      const float* pair_w, const int32_t* topk_idx, int64_t T, int k, int d, int E, Elem* dy_perm,
+                      float* dw, float* dlogits, hipStream_t s) {
+  const int64_t vec_per_row = (int64_t)d * sizeof(Elem) / 16;
+  const int64_t blocks = ceil_div(T, kThreads / kWave);
+  k_combine_bwd<Elem><<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)dout, (const u32x4*)y_perm, max_rows,
+                                                           pair_row, pair_w, topk_idx, T, k, E, vec_per_row,
+                                                           (u32x4*)dy_perm, dw, dlogits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_combine_bwd_bf16(const bf16_t* dout, const bf16_t* y_perm, int64_t max_rows,
                                   const int32_t* pair_row, const float* pair_w, const int32_t* topk_idx, int64_t T,
                                   int k, int d, int E, bf16_t* dy_perm, float* dw, float* dlogits, hipStream_t s) {
-  const int64_t vec_per_row = (int64_t)d * 2 / 16;
-  const int64_t blocks = ceil_div(T, kThreads / kWave);
-  k_combine_bwd<<<(unsigned)blocks, kThreads, 0, s>>>((const u32x4*)dout, (const u32x4*)y_perm, max_rows, pair_row,
-                                                     pair_w, topk_idx, T, k, E, vec_per_row, (u32x4*)dy_perm, dw,
-                                                     dlogits);
-  return hipGetLastError();
+  return launch_bwd<bf16_t>(dout, y_perm, max_rows, pair_row, pair_w, topk_idx, T, k, d, E, dy_perm, dw, dlogits, s);
+}
+
+hipError_t launch_combine_bwd_f32(const float* dout, const float* y_perm, int64_t max_rows,
+                                  const int32_t* pair_row, const float* pair_w, const int32_t* topk_idx, int64_t T,
+                                  int k, int d, int E, float* dy_perm, float* dw, float* dlogits, hipStream_t s) {
+  return launch_bwd<float>(dout, y_perm, max_rows, pair_row, pair_w, topk_idx, T, k, d, E, dy_perm, dw, dlogits, s);
 }
 
 hipError_t launch_zero_unrouted_bf16(const int32_t* pair_row, int64_t max_rows, int64_t T, int d, bf16_t* out,

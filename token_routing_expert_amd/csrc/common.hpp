@@ -289,4 +289,18 @@ hipError_t launch_zero_bf16(bf16_t* p, int64_t n, hipStream_t s);
 hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, int M, const bf16_t* b, int ldb, int N,
                              const int32_t* expert_offsets, int64_t max_rows, int E, bf16_t* dw, hipStream_t s);
 
+// ---- backward (float32): the same steps on float32 rows and weights ----
+hipError_t launch_gate_up_save_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                   int d, int I, const float* w_gate_up, float* h, float* gu, hipStream_t s);
+hipError_t launch_combine_bwd_f32(const float* dout, const float* y_perm, int64_t max_rows,
+                                  const int32_t* pair_row, const float* pair_w, const int32_t* topk_idx, int64_t T,
+                                  int k, int d, int E, float* dy_perm, float* dw, float* dlogits, hipStream_t s);
+hipError_t launch_down_dgrad_swiglu_f32(const float* dy, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                        int d, int I, const float* w_down, const float* gu, float* dgu,
+                                        hipStream_t s);
+hipError_t launch_gate_up_dgrad_f32(const float* dgu, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                    int d, int I, const float* w_gate_up, float* dx_perm, hipStream_t s);
+hipError_t launch_wgrad_f32(const float* a, int lda, int M, const float* b, int ldb, int N,
+                            const int32_t* expert_offsets, int64_t max_rows, int E, float* dw, hipStream_t s);
+
 }  // namespace tre

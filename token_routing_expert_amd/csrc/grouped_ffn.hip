@@ -1263,31 +1263,73 @@ int persistent_grid(int64_t max_rows, int E, int bm, int n_tiles, int occ) {
 }
 
 // ---- float32 path -----------------------------------------------------------
-// Tiles of 64 grouped rows x 128 weight columns in k-stages of 32, four waves
-// (2 x 2) of 32 rows x 64 columns, each two 32 x 32 blocks of
-// v_mfma_f32_32x32x2_f32.  That MFMA takes A (32 x 2) with A[i][k] in lane
-// i + 32 k and B (2 x 32) with B[k][j] in lane j + 32 k, and register q of
-// lane l of its 32 x 32 float32 result holds row 8 (q / 4) + 4 (l / 32) +
-// q % 4, column l % 32.  A gate/up tile takes 64 gate columns and the
-// matching 64 up columns, and a wave's two blocks are gate columns j and up
-// columns j, so each SwiGLU pair meets in one lane and register.  Stages are
-// double-buffered in LDS: the next stage's global loads are in registers
-// while the current one is multiplied, and one barrier a stage separates
-// the two.  One workgroup per (row tile, column tile); row tiles are
-// numbered expert by expert from the device offsets, and the rows of a
-// tile's last partial block load as zeros and are not stored.
+// Tiles of 64 output rows x 128 columns in k-stages of 32, four waves (2 x 2)
+// of 32 rows x 64 columns, each two 32 x 32 blocks of v_mfma_f32_32x32x2_f32.
+// That MFMA takes A (32 x 2) with A[i][k] in lane i + 32 k and B (2 x 32)
+// with B[k][j] in lane j + 32 k, and register q of lane l of its 32 x 32
+// float32 result holds row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32.
+// Stages are double-buffered in LDS: the next stage's global loads are in
+// registers while the current one is multiplied, and one barrier a stage
+// separates the two.  Rows past an operand's end load as zeros.
+//
+// Operands in LDS, by how they lie in memory:
+//   A rows  [64][33]  (the grouped rows, k contiguous);
+//   A^T     [32][96]  (the weight gradient's contraction over an expert's
+//                      rows: k = row, the output rows contiguous);
+//   B       [32][160] (weights [K][ldw], columns contiguous);
+//   B^T     [128][33] (weights read as [N][K], k contiguous: the backward's
+//                      products with Wd^T and Wgu^T).
+// The pads put the two k-halves of an MFMA operand (lanes 0-31, 32-63) on
+// different LDS banks.
 constexpr int kF32Rows = 64, kF32Cols = 128, kF32K = 32;
+constexpr int kF32Epi = 0, kF32Swiglu = 1, kF32SwigluSave = 2, kF32SwigluBwd = 3;
 
-template <bool SWIGLU>
+struct F32Stage {
+  static constexpr int LDA = kF32K + 1, LDAT = kF32Rows + 32, LDB = kF32Cols + 32, LDBT = kF32K + 1;
+  static constexpr int A_FLOATS = kF32Rows * LDA > kF32K * LDAT ? kF32Rows * LDA : kF32K * LDAT;
+  static constexpr int B_FLOATS = kF32K * LDB > kF32Cols * LDBT ? kF32K * LDB : kF32Cols * LDBT;
+};
+
+// One stage's MFMAs: a wave's rows 32 wm.., its two column blocks cb0, cb1.
+template <bool AT, bool BT>
+__device__ __forceinline__ void f32_stage_mma(const float* sA, const float* sB, int wm, int cb0, int cb1, int lane,
+                                              f32x16& acc0, f32x16& acc1) {
+  typedef F32Stage S;
+  const int i = 32 * wm + lane % 32, kh = lane / 32, j = lane % 32;
+#pragma unroll
+  for (int kk = 0; kk < kF32K / 2; ++kk) {
+    const int k = 2 * kk + kh;
+    const float av = AT ? sA[k * S::LDAT + i] : sA[i * S::LDA + k];
+    const float b0 = BT ? sB[(cb0 + j) * S::LDBT + k] : sB[k * S::LDB + cb0 + j];
+    const float b1 = BT ? sB[(cb1 + j) * S::LDBT + k] : sB[k * S::LDB + cb1 + j];
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
+  }
+}
+
+// The grouped products: row tiles of each expert's grouped rows, numbered
+// expert by expert from the device offsets, times column tiles.
+//   kF32Epi:        Out = A W                            (N columns)
+//   kF32Swiglu:     Out = silu(A Wg) * (A Wu)            (W = [Wg | Wu], 2N columns; a tile takes 64 gate
+//                                                          columns and the matching 64 up columns, and a
+//                                                          wave's two blocks are gate columns j and up
+//                                                          columns j, so each pair meets in one register)
+//   kF32SwigluSave: as kF32Swiglu, and Out2 = [A Wg | A Wu] (row stride 2N)
+//   kF32SwigluBwd:  Out = [dg | du] (row stride 2N) from dh = A W and Aux = [g | u]:
+//                   dg = dh u s (1 + g (1 - s)), du = dh g s, s = sigmoid(g)
+// BT: W is read as [N][K] (row n holds column n of the product's weight).
+template <int EPI, bool BT>
 __global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restrict__ A,
                                                           const int32_t* __restrict__ offsets, int64_t max_rows,
                                                           int E, int K, int N, const float* __restrict__ W,
-                                                          float* __restrict__ Out) {
+                                                          float* __restrict__ Out, float* __restrict__ Out2,
+                                                          const float* __restrict__ Aux) {
+  constexpr bool GU = EPI == kF32Swiglu || EPI == kF32SwigluSave;   // gate/up column pairs
+  static_assert(!(GU && BT), "the gate/up weight is read as [K][2N]");
   constexpr int BM = kF32Rows, BN = kF32Cols, BK = kF32K;
-  constexpr int LDA = BK + 1;   // a row of A in LDS (the pad spreads a wave's rows over the banks)
-  constexpr int LDB = BN + 32;  // a k-row of B in LDS (the pad puts k and k + 1 on different banks)
-  __shared__ float sA[2][BM * LDA];
-  __shared__ __attribute__((aligned(16))) float sB[2][BK * LDB];
+  typedef F32Stage S;
+  __shared__ float sA[2][S::A_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sB[2][S::B_FLOATS];
   __shared__ int s_wave[4];
   __shared__ int s_tile[3];  // expert, first grouped row, rows
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -1312,13 +1354,13 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restric
   }
   __syncthreads();
   const int e = s_tile[0], r0 = s_tile[1], rows = s_tile[2];
-  const int ldw = SWIGLU ? 2 * N : N;
-  const int n0 = (int)blockIdx.y * (SWIGLU ? BN / 2 : BN);
-  const float* We = W + (int64_t)e * K * ldw;
+  const int ldw = BT ? K : GU ? 2 * N : N;
+  const int n0 = (int)blockIdx.y * (GU ? BN / 2 : BN);
+  const float* We = W + (int64_t)e * K * (GU ? 2 * N : N);
 
-  // the global column of LDS column cb (a multiple of 4), or -1 past N
+  // the weight column of LDS column cb (a multiple of 4), or -1 past N
   auto gcol = [&](int cb) -> int {
-    if (SWIGLU) return cb < BN / 2 ? n0 + cb : N + n0 + cb - BN / 2;
+    if (GU) return cb < BN / 2 ? n0 + cb : N + n0 + cb - BN / 2;
     return n0 + cb < N ? n0 + cb : -1;
   };
   f32x4 ra[2], rb[4];
@@ -1330,8 +1372,14 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restric
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, k = q / 32, col = gcol(4 * (q % 32));
-      rb[i] = col >= 0 ? *(const f32x4*)(We + (int64_t)(k0 + k) * ldw + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int q = tid + 256 * i;
+      if (BT) {   // 128 weight rows (the product's columns) x 32 k
+        const int n = q / 8, c = 4 * (q % 8);
+        rb[i] = n0 + n < N ? *(const f32x4*)(We + (int64_t)(n0 + n) * ldw + k0 + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {    // 32 k-rows x 128 columns
+        const int k = q / 32, col = gcol(4 * (q % 32));
+        rb[i] = col >= 0 ? *(const f32x4*)(We + (int64_t)(k0 + k) * ldw + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   };
   auto store = [&](int buf) {
@@ -1339,33 +1387,32 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restric
     for (int i = 0; i < 2; ++i) {
       const int q = tid + 256 * i, row = q / 8, c = 4 * (q % 8);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sA[buf][row * LDA + c + j] = ra[i][j];
+      for (int j = 0; j < 4; ++j) sA[buf][row * S::LDA + c + j] = ra[i][j];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = tid + 256 * i;
-      *(f32x4*)&sB[buf][(q / 32) * LDB + 4 * (q % 32)] = rb[i];
+      if (BT) {
+        const int n = q / 8, c = 4 * (q % 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sB[buf][n * S::LDBT + c + j] = rb[i][j];
+      } else {
+        *(f32x4*)&sB[buf][(q / 32) * S::LDB + 4 * (q % 32)] = rb[i];
+      }
     }
   };
   // a wave's two column blocks in LDS
-  const int cb0 = SWIGLU ? 32 * wn : 64 * wn, cb1 = SWIGLU ? BN / 2 + 32 * wn : 64 * wn + 32;
+  const int cb0 = GU ? 32 * wn : 64 * wn, cb1 = GU ? BN / 2 + 32 * wn : 64 * wn + 32;
   f32x16 acc0 = {}, acc1 = {};
   const int nk = K / BK;
   load(0);
   store(0);
   __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) load((s + 1) * BK);
-    const float* a = &sA[buf][(32 * wm + lane % 32) * LDA + lane / 32];
-    const float* b = &sB[buf][(lane / 32) * LDB + lane % 32];
-#pragma unroll
-    for (int kk = 0; kk < BK / 2; ++kk) {
-      const float av = a[2 * kk];
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[2 * kk * LDB + cb0], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[2 * kk * LDB + cb1], acc1, 0, 0, 0);
-    }
-    if (s + 1 < nk) store(buf ^ 1);
+  for (int st = 0; st < nk; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nk) load((st + 1) * BK);
+    f32_stage_mma<false, BT>(sA[buf], sB[buf], wm, cb0, cb1, lane, acc0, acc1);
+    if (st + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
   // epilogue: register q of this lane is row 8 (q / 4) + 4 (lane / 32) + q % 4 of the wave's 32 rows
@@ -1374,14 +1421,104 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restric
   for (int q = 0; q < 16; ++q) {
     const int r = 32 * wm + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
     if (r >= rows) continue;
-    float* o = Out + (int64_t)(r0 + r) * N;
-    if (SWIGLU) {
+    const int64_t gr = r0 + r;
+    if constexpr (GU) {
+      const int n = n0 + 32 * wn + col;
       const float g = acc0[q], up = acc1[q];
-      o[n0 + 32 * wn + col] = g / (1.f + expf(-g)) * up;
+      Out[gr * N + n] = g / (1.f + expf(-g)) * up;
+      if (EPI == kF32SwigluSave) {
+        Out2[gr * 2 * N + n] = g;
+        Out2[gr * 2 * N + N + n] = up;
+      }
     } else {
-      if (n0 + cb0 + col < N) o[n0 + cb0 + col] = acc0[q];
-      if (n0 + cb1 + col < N) o[n0 + cb1 + col] = acc1[q];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int n = n0 + (b ? cb1 : cb0) + col;
+        const float v = b ? acc1[q] : acc0[q];
+        if (n >= N) continue;
+        if (EPI == kF32SwigluBwd) {
+          const float g = Aux[gr * 2 * N + n], up = Aux[gr * 2 * N + N + n];
+          const float sg = 1.f / (1.f + expf(-g));
+          Out[gr * 2 * N + n] = v * up * sg * (1.f + g * (1.f - sg));
+          Out[gr * 2 * N + N + n] = v * g * sg;
+        } else {
+          Out[gr * N + n] = v;
+        }
+      }
     }
+  }
+}
+
+// Per-expert weight gradients dW[e] = A_e^T B_e [M][N] ("Expert parallelism",
+// "Combining with FSDP2": an expert's gradient sums over every row it served,
+// and is zero when it served none), the contraction over expert e's grouped
+// rows (A [rows][lda], B [rows][ldb]) in stages of 32 rows; one workgroup per
+// (expert, 64-row block, 128-column block) of dW.
+__global__ __launch_bounds__(256) void k_wgrad_f32(const float* __restrict__ A, int lda, int M,
+                                                   const float* __restrict__ B, int ldb, int N,
+                                                   const int32_t* __restrict__ offsets, int64_t max_rows,
+                                                   int m_tiles, int n_tiles, float* __restrict__ dW) {
+  constexpr int BM = kF32Rows, BN = kF32Cols, BK = kF32K;
+  typedef F32Stage S;
+  __shared__ __attribute__((aligned(16))) float sA[2][S::A_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sB[2][S::B_FLOATS];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const int per_e = m_tiles * n_tiles;
+  const int e = (int)blockIdx.x / per_e, rem = (int)blockIdx.x % per_e;
+  const int m0 = (rem % m_tiles) * BM, n0 = (rem / m_tiles) * BN;
+  MOE_DCHECK(0 <= offsets[e] && offsets[e] <= offsets[e + 1] && offsets[e + 1] <= max_rows);
+  const int64_t lo = clampi<int64_t>(offsets[e], 0, max_rows);
+  const int cnt = (int)(clampi<int64_t>(offsets[e + 1], lo, max_rows) - lo);
+
+  f32x4 ra[2], rb[4];
+  auto load = [&](int k0) {   // rows k0 .. k0 + 31 of the expert
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i, kr = q / 16, m = m0 + 4 * (q % 16);
+      ra[i] = (k0 + kr < cnt && m < M) ? *(const f32x4*)(A + (lo + k0 + kr) * lda + m) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, kr = q / 32, n = n0 + 4 * (q % 32);
+      rb[i] = (k0 + kr < cnt && n < N) ? *(const f32x4*)(B + (lo + k0 + kr) * ldb + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i;
+      *(f32x4*)&sA[buf][(q / 16) * S::LDAT + 4 * (q % 16)] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      *(f32x4*)&sB[buf][(q / 32) * S::LDB + 4 * (q % 32)] = rb[i];
+    }
+  };
+  const int cb0 = 64 * wn, cb1 = 64 * wn + 32;
+  f32x16 acc0 = {}, acc1 = {};
+  const int nk = (cnt + BK - 1) / BK;
+  if (nk > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nk; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nk) load((st + 1) * BK);
+    f32_stage_mma<true, false>(sA[buf], sB[buf], wm, cb0, cb1, lane, acc0, acc1);
+    if (st + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+  float* out = dW + (int64_t)e * M * N;
+  const int col = lane % 32;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int m = m0 + 32 * wm + 8 * (q / 4) + 4 * (lane / 32) + q % 4;
+    if (m >= M) continue;
+    if (n0 + cb0 + col < N) out[(int64_t)m * N + n0 + cb0 + col] = acc0[q];
+    if (n0 + cb1 + col < N) out[(int64_t)m * N + n0 + cb1 + col] = acc1[q];
   }
 }
 
@@ -1710,19 +1847,54 @@ static unsigned f32_row_tiles(int64_t max_rows, int E) {
   return (unsigned)(max_rows / kF32Rows + (E < max_rows ? E : max_rows));
 }
 
+template <int EPI, bool BT>
+static hipError_t launch_f32(const float* a, const int32_t* offsets, int64_t max_rows, int E, int K, int N,
+                             const float* w, float* out, hipStream_t s, float* out2 = nullptr,
+                             const float* aux = nullptr) {
+  constexpr bool GU = EPI == kF32Swiglu || EPI == kF32SwigluSave;
+  const dim3 g(f32_row_tiles(max_rows, E), (unsigned)ceil_div(N, GU ? kF32Cols / 2 : kF32Cols));
+  if (g.x == 0 || g.y == 0) return hipSuccess;
+  if (K % kF32K != 0) return hipErrorInvalidValue;
+  k_grouped_gemm_f32<EPI, BT><<<g, 256, 0, s>>>(a, offsets, max_rows, E, K, N, w, out, out2, aux);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
                               int d, int I, const float* w_gate_up, float* h, hipStream_t s) {
-  const dim3 g(f32_row_tiles(max_rows, E), (unsigned)ceil_div(I, kF32Cols / 2));
-  if (g.x == 0 || g.y == 0) return hipSuccess;
-  k_grouped_gemm_f32<true><<<g, 256, 0, s>>>(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h);
-  return hipGetLastError();
+  return launch_f32<kF32Swiglu, false>(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s);
 }
 
 hipError_t launch_down_f32(const float* h, const int32_t* expert_offsets, int64_t max_rows, int E, int d,
                            int I, const float* w_down, float* y_perm, hipStream_t s) {
-  const dim3 g(f32_row_tiles(max_rows, E), (unsigned)ceil_div(d, kF32Cols));
-  if (g.x == 0 || g.y == 0) return hipSuccess;
-  k_grouped_gemm_f32<false><<<g, 256, 0, s>>>(h, expert_offsets, max_rows, E, I, d, w_down, y_perm);
+  return launch_f32<kF32Epi, false>(h, expert_offsets, max_rows, E, I, d, w_down, y_perm, s);
+}
+
+hipError_t launch_gate_up_save_f32(const float* x_perm, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                   int d, int I, const float* w_gate_up, float* h, float* gu, hipStream_t s) {
+  return launch_f32<kF32SwigluSave, false>(x_perm, expert_offsets, max_rows, E, d, I, w_gate_up, h, s, gu);
+}
+
+hipError_t launch_down_dgrad_swiglu_f32(const float* dy, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                        int d, int I, const float* w_down, const float* gu, float* dgu,
+                                        hipStream_t s) {
+  // dh = dy Wd^T: Wd [I][d] is the [N][K] weight of a product with K = d, N = I
+  return launch_f32<kF32SwigluBwd, true>(dy, expert_offsets, max_rows, E, d, I, w_down, dgu, s, nullptr, gu);
+}
+
+hipError_t launch_gate_up_dgrad_f32(const float* dgu, const int32_t* expert_offsets, int64_t max_rows, int E,
+                                    int d, int I, const float* w_gate_up, float* dx_perm, hipStream_t s) {
+  // dx = [dg | du] Wgu^T: Wgu [d][2I] is the [N][K] weight of a product with K = 2I, N = d
+  return launch_f32<kF32Epi, true>(dgu, expert_offsets, max_rows, E, 2 * I, d, w_gate_up, dx_perm, s);
+}
+
+hipError_t launch_wgrad_f32(const float* a, int lda, int M, const float* b, int ldb, int N,
+                            const int32_t* expert_offsets, int64_t max_rows, int E, float* dw, hipStream_t s) {
+  if (M % 4 != 0 || N % 4 != 0 || lda < M || ldb < N) return hipErrorInvalidValue;
+  const int m_tiles = (int)ceil_div(M, kF32Rows), n_tiles = (int)ceil_div(N, kF32Cols);
+  const int64_t blocks = (int64_t)E * m_tiles * n_tiles;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  k_wgrad_f32<<<(unsigned)blocks, 256, 0, s>>>(a, lda, M, b, ldb, N, expert_offsets, max_rows, m_tiles, n_tiles, dw);
   return hipGetLastError();
 }
 
