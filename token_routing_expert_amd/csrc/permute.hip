@@ -38,6 +38,37 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Adds 1 to cnt[e] (LDS) for every expert id e in [0, E) among
+// pair_expert[lo, hi), the workgroup's threads striding over the range.  A
+// thread's ids are read kCountBatch at a time with every load in flight
+// together (an id's load and its count in turn would wait a full memory
+// round trip per id); lanes past hi re-read pair_expert[lo] and count
+// nothing.
+constexpr int kCountBatch = 8;   // (the asm below names each of the 8)
+
+__device__ __forceinline__ void count_ids(const int32_t* __restrict__ pair_expert, int64_t lo, int64_t hi, int E,
+                                          int* cnt) {
+  for (int64_t q0 = lo + threadIdx.x; q0 < hi; q0 += (int64_t)kCountBatch * kThreads) {
+    int ev[kCountBatch];
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) {
+      const int64_t q = q0 + (int64_t)u * kThreads;
+      ev[u] = pair_expert[q < hi ? q : lo];
+    }
+    // (without this the compiler waits for the first id before issuing the
+    // other loads, to test it early)
+    asm volatile("" : "+v"(ev[0]), "+v"(ev[1]), "+v"(ev[2]), "+v"(ev[3]), "+v"(ev[4]), "+v"(ev[5]), "+v"(ev[6]),
+                 "+v"(ev[7]));
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) {
+      const int64_t q = q0 + (int64_t)u * kThreads;
+      if (q >= hi) continue;
+      MOE_DCHECK(ev[u] >= -1 && ev[u] < E);   // an expert id, or -1 for a masked pair
+      if (ev[u] >= 0 && ev[u] < E) atomicAdd(&cnt[ev[u]], 1);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_perm_hist(const int32_t* __restrict__ pair_expert, int64_t P,
                                                         int E, int chunk_pairs, int32_t* __restrict__ chunk_count,
                                                         int32_t* __restrict__ sched) {
@@ -47,14 +78,7 @@ __global__ __launch_bounds__(kThreads) void k_perm_hist(const int32_t* __restric
   if (tid < E) cnt[tid] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * chunk_pairs;
-  for (int i = tid; i < chunk_pairs; i += kThreads) {
-    const int64_t p = base + i;
-    if (p < P) {
-      const int e = pair_expert[p];
-      MOE_DCHECK(e >= -1 && e < E);   // an expert id, or -1 for a masked pair
-      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
-  }
+  count_ids(pair_expert, base, min(P, base + chunk_pairs), E, cnt);
   __syncthreads();
   if (tid < E) chunk_count[(int64_t)blockIdx.x * E + tid] = cnt[tid];
 }
@@ -423,11 +447,7 @@ __global__ __launch_bounds__(kThreads) void k_perm_rows(
     }
   }
   // ... and in this chunk
-#pragma unroll 4
-  for (int64_t q = (int64_t)c0 * chunk_pairs + tid; q < p0; q += kThreads) {
-    const int eq = pair_expert[q];
-    if (eq >= 0 && eq < E) atomicAdd(&s_before[eq], 1);
-  }
+  count_ids(pair_expert, (int64_t)c0 * chunk_pairs, p0, E, s_before);
   __syncthreads();
   if (chunk_base) {
     if (tid < E) running[tid] = s_before[tid];
