@@ -1263,41 +1263,50 @@ int persistent_grid(int64_t max_rows, int E, int bm, int n_tiles, int occ) {
 }
 
 // ---- float32 path -----------------------------------------------------------
-// Tiles of 64 output rows x 128 columns in k-stages of 32, four waves (2 x 2)
-// of 32 rows x 64 columns, each two 32 x 32 blocks of v_mfma_f32_32x32x2_f32.
+// Tiles of 64 output rows x 128 columns in k-stages of 64 (the weight
+// gradients: stages of 32 rows), four waves (2 x 2) of 32 rows x 64 columns,
+// each two 32 x 32 blocks of v_mfma_f32_32x32x2_f32.
 // That MFMA takes A (32 x 2) with A[i][k] in lane i + 32 k and B (2 x 32)
 // with B[k][j] in lane j + 32 k, and register q of lane l of its 32 x 32
 // float32 result holds row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32.
 // Stages are double-buffered in LDS: the next stage's global loads are in
 // registers while the current one is multiplied, and one barrier a stage
-// separates the two.  Rows past an operand's end load as zeros.
+// separates the two.  At the sizes this path serves a stage waits about one
+// memory round trip for its loads, so the products take deep stages: half as
+// many round trips as 32-wide ones.  Rows past an operand's end load as zeros.
 //
 // Operands in LDS, by how they lie in memory:
-//   A rows  [64][33]  (the grouped rows, k contiguous);
+//   A rows  [64][97]  (the grouped rows, k contiguous);
 //   A^T     [32][96]  (the weight gradient's contraction over an expert's
 //                      rows: k = row, the output rows contiguous);
-//   B       [32][160] (weights [K][ldw], columns contiguous);
-//   B^T     [128][33] (weights read as [N][K], k contiguous: the backward's
+//   B       [64][160] (weights [K][ldw], columns contiguous; the weight
+//                      gradient's second operand: [32][160]);
+//   B^T     [128][97] (weights read as [N][K], k contiguous: the backward's
 //                      products with Wd^T and Wgu^T).
 // The pads put the two k-halves of an MFMA operand (lanes 0-31, 32-63) on
-// different LDS banks.
-constexpr int kF32Rows = 64, kF32Cols = 128, kF32K = 32;
+// different LDS banks (64 banks of 4 bytes: row i of a k-contiguous operand
+// starts at bank 33 i mod 64).
+constexpr int kF32Rows = 64, kF32Cols = 128;
+constexpr int kF32K = 64;    // k-stage depth of the products
+constexpr int kF32WK = 32;   // rows per stage of the weight gradients' contraction
 constexpr int kF32Epi = 0, kF32Swiglu = 1, kF32SwigluSave = 2, kF32SwigluBwd = 3;
 
 struct F32Stage {
-  static constexpr int LDA = kF32K + 1, LDAT = kF32Rows + 32, LDB = kF32Cols + 32, LDBT = kF32K + 1;
-  static constexpr int A_FLOATS = kF32Rows * LDA > kF32K * LDAT ? kF32Rows * LDA : kF32K * LDAT;
+  static constexpr int LDA = kF32K + 33, LDAT = kF32Rows + 32, LDB = kF32Cols + 32, LDBT = kF32K + 33;
+  static constexpr int A_FLOATS = kF32Rows * LDA;                                  // A rows
   static constexpr int B_FLOATS = kF32K * LDB > kF32Cols * LDBT ? kF32K * LDB : kF32Cols * LDBT;
+  static constexpr int WA_FLOATS = kF32WK * LDAT, WB_FLOATS = kF32WK * LDB;        // the weight gradients
 };
 
-// One stage's MFMAs: a wave's rows 32 wm.., its two column blocks cb0, cb1.
-template <bool AT, bool BT>
+// One stage's MFMAs over KD k-values: a wave's rows 32 wm.., its two column
+// blocks cb0, cb1.
+template <bool AT, bool BT, int KD>
 __device__ __forceinline__ void f32_stage_mma(const float* sA, const float* sB, int wm, int cb0, int cb1, int lane,
                                               f32x16& acc0, f32x16& acc1) {
   typedef F32Stage S;
   const int i = 32 * wm + lane % 32, kh = lane / 32, j = lane % 32;
 #pragma unroll
-  for (int kk = 0; kk < kF32K / 2; ++kk) {
+  for (int kk = 0; kk < KD / 2; ++kk) {
     const int k = 2 * kk + kh;
     const float av = AT ? sA[k * S::LDAT + i] : sA[i * S::LDA + k];
     const float b0 = BT ? sB[(cb0 + j) * S::LDBT + k] : sB[k * S::LDB + cb0 + j];
@@ -1363,20 +1372,23 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restric
     if (GU) return cb < BN / 2 ? n0 + cb : N + n0 + cb - BN / 2;
     return n0 + cb < N ? n0 + cb : -1;
   };
-  f32x4 ra[2], rb[4];
+  // a stage: 64 rows x BK of A (BK / 4 vectors a row), and BK k-rows x 128
+  // columns of W (or, BT, 128 weight rows x BK)
+  constexpr int VA = BM * BK / 4 / 256, VB = BK * BN / 4 / 256, VR = BK / 4;   // vectors a thread / a k-run
+  f32x4 ra[VA], rb[VB];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i, row = q / 8, c = 4 * (q % 8);
+    for (int i = 0; i < VA; ++i) {
+      const int q = tid + 256 * i, row = q / VR, c = 4 * (q % VR);
       ra[i] = row < rows ? *(const f32x4*)(A + (int64_t)(r0 + row) * K + k0 + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < VB; ++i) {
       const int q = tid + 256 * i;
-      if (BT) {   // 128 weight rows (the product's columns) x 32 k
-        const int n = q / 8, c = 4 * (q % 8);
+      if (BT) {   // 128 weight rows (the product's columns) x BK k
+        const int n = q / VR, c = 4 * (q % VR);
         rb[i] = n0 + n < N ? *(const f32x4*)(We + (int64_t)(n0 + n) * ldw + k0 + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-      } else {    // 32 k-rows x 128 columns
+      } else {    // BK k-rows x 128 columns
         const int k = q / 32, col = gcol(4 * (q % 32));
         rb[i] = col >= 0 ? *(const f32x4*)(We + (int64_t)(k0 + k) * ldw + col) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -1384,16 +1396,16 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restric
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i, row = q / 8, c = 4 * (q % 8);
+    for (int i = 0; i < VA; ++i) {
+      const int q = tid + 256 * i, row = q / VR, c = 4 * (q % VR);
 #pragma unroll
       for (int j = 0; j < 4; ++j) sA[buf][row * S::LDA + c + j] = ra[i][j];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < VB; ++i) {
       const int q = tid + 256 * i;
       if (BT) {
-        const int n = q / 8, c = 4 * (q % 8);
+        const int n = q / VR, c = 4 * (q % VR);
 #pragma unroll
         for (int j = 0; j < 4; ++j) sB[buf][n * S::LDBT + c + j] = rb[i][j];
       } else {
@@ -1411,7 +1423,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(const float* __restric
   for (int st = 0; st < nk; ++st) {
     const int buf = st & 1;
     if (st + 1 < nk) load((st + 1) * BK);
-    f32_stage_mma<false, BT>(sA[buf], sB[buf], wm, cb0, cb1, lane, acc0, acc1);
+    f32_stage_mma<false, BT, BK>(sA[buf], sB[buf], wm, cb0, cb1, lane, acc0, acc1);
     if (st + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
@@ -1458,10 +1470,10 @@ __global__ __launch_bounds__(256) void k_wgrad_f32(const float* __restrict__ A, 
                                                    const float* __restrict__ B, int ldb, int N,
                                                    const int32_t* __restrict__ offsets, int64_t max_rows,
                                                    int m_tiles, int n_tiles, float* __restrict__ dW) {
-  constexpr int BM = kF32Rows, BN = kF32Cols, BK = kF32K;
+  constexpr int BM = kF32Rows, BN = kF32Cols, BK = kF32WK;
   typedef F32Stage S;
-  __shared__ __attribute__((aligned(16))) float sA[2][S::A_FLOATS];
-  __shared__ __attribute__((aligned(16))) float sB[2][S::B_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sA[2][S::WA_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sB[2][S::WB_FLOATS];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;
   const int per_e = m_tiles * n_tiles;
@@ -1507,7 +1519,7 @@ __global__ __launch_bounds__(256) void k_wgrad_f32(const float* __restrict__ A, 
   for (int st = 0; st < nk; ++st) {
     const int buf = st & 1;
     if (st + 1 < nk) load((st + 1) * BK);
-    f32_stage_mma<true, false>(sA[buf], sB[buf], wm, cb0, cb1, lane, acc0, acc1);
+    f32_stage_mma<true, false, BK>(sA[buf], sB[buf], wm, cb0, cb1, lane, acc0, acc1);
     if (st + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
