@@ -425,7 +425,10 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
   if (E <= 16) return launch<16, 1>(logits, T, E, k, topk_idx, topk_w, s);
   if (E <= 32) return launch<32, 1>(logits, T, E, k, topk_idx, topk_w, s);
   if (E <= 64) return launch<64, 1>(logits, T, E, k, topk_idx, topk_w, s);
-  if (E <= 128) return launch<64, 2>(logits, T, E, k, topk_idx, topk_w, s);
+  // 65-128 experts: groups of 16 lanes holding 8 logits each (four tokens a
+  // wave): each pick is a local maximum over a lane's keys and four shuffle
+  // steps, instead of six over a whole wave per token
+  if (E <= 128) return launch<16, 8>(logits, T, E, k, topk_idx, topk_w, s);
   return launch<64, 4>(logits, T, E, k, topk_idx, topk_w, s);
 }
 
