@@ -7,7 +7,8 @@
 // softmax over the E logits renormalised over the k picks, which equals
 // exp(l_j - l_0) / sum_i exp(l_i - l_0) over the picks.
 //
-// Design: a group of G lanes (a whole wave64 when E > 32) owns one token and
+// Design: a group of G lanes (16 for 65-128 experts, a whole wave64 for 33-64
+// and for more than 128) owns one token and
 // holds its logits in registers, S = ceil(E / G) per lane.  Each logit is
 // turned into a 64-bit key that orders as the selection rule does (logit in
 // the high word, mapped to an unsigned order; the complement of the expert
